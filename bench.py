@@ -1,0 +1,310 @@
+"""Benchmark of one MoE layer's data path on one MI355X: routing layout +
+dispatch + combine, timed through the C ABI.
+
+A step is one pass of the whole path over one batch: moe_get_layout (3
+kernels), moe_dispatch (1 kernel), moe_combine (1 kernel), with every input
+already resident in HBM.  The expert computation between dispatch and combine
+is not part of the path; a stand-in expert output (the dequantized dispatched
+rows, or the dispatched bf16 rows) is prepared once, untimed.
+
+Bytes are counted in the form the DeepEP issue "#84 Questions on Profiling
+dispatch_t ..." prints bandwidth (bytes / 1e9 / t), counting every copy
+including those a rank sends to itself: dispatch N * (H * s + 4 [int8 scale]),
+combine N * 2H, with N routed copies and s = 1 (int8) or 2 (bf16) bytes; the
+closed form is the one of "Wide-EP / DBO / DeepEP hardware cliff", A short
+illustrative example (tokens per rank x k x d x s).
+
+Output: one JSON line (see main()).  --gpus above 1 is refused: the path runs
+on one GPU.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published peak
+METRIC = "dispatch+combine µs/layer and achieved HBM GB/s (% of peak), T=4096 H=7168 k=8"
+DEFAULT_WORKLOAD = 2
+
+
+def comm_bytes(n_rows, hidden, payload_bytes, scale_bytes):
+    """Bytes a dispatch or combine moves in the printed-bandwidth accounting:
+    every routed copy once, self copies included."""
+    return int(n_rows) * (int(hidden) * int(payload_bytes) + int(scale_bytes))
+
+
+def dispatch_comm_bytes(n_rows, hidden, quant_mode):
+    return comm_bytes(n_rows, hidden, 2 if quant_mode == 0 else 1, 4 if quant_mode == 2 else 0)
+
+
+def combine_comm_bytes(n_rows, hidden):
+    return comm_bytes(n_rows, hidden, 2, 0)
+
+
+def dispatch_hbm_bytes(T, H, K, n_rows, n_tok_sending, quant_mode, smooth):
+    """Algorithmic HBM bytes of one dispatch launch: each sending token's row is read once,
+    every routed copy written once, plus the slot map and the per-row scale."""
+    rd = n_tok_sending * 2 * H + T * K * 4 + (4 * H if smooth else 0)
+    wr = n_rows * (H * (2 if quant_mode == 0 else 1) + (4 if quant_mode == 2 else 0))
+    return rd + wr
+
+
+def combine_hbm_bytes(T, H, K, n_rows, n_tok_ori):
+    """Algorithmic HBM bytes of one combine launch: every routed expert-output row read
+    once, ori_x for tokens with a copy/constant slot, the slot map, one bf16 row written per token."""
+    return n_rows * 2 * H + n_tok_ori * 2 * H + T * K * 12 + T * 2 * H
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "combine": ["combine_moe_get_amd/csrc/combine.hip", "combine_moe_get_amd/csrc/moe_internal.hpp"],
+    "dispatch": ["combine_moe_get_amd/csrc/dispatch.hip", "combine_moe_get_amd/csrc/moe_internal.hpp"],
+}
+
+
+def counter_traffic(kernel, workload_name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_name}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_h or not m_b or m_h.group(1) != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(inp, target_seconds):
+    """The oracle, as it stands (single-threaded C), timed on this host over whole
+    layout + dispatch + combine passes of the same workload."""
+    import oracle
+
+    c = inp["cfg"]
+    sh = oracle.make_shape(c["T"], c["H"], c["K"], c["E"], c["P"], c["Z"], c["C"], c["Kc"], c["num_max"])
+    reps, total_comm, dt = 0, 0, 0.0
+    while dt < target_seconds:
+        a = time.perf_counter()
+        lo = oracle.layout(sh, inp["topk_idx"], inp["mask"])
+        oracle.dispatch(sh, c["quant_mode"], inp["x"], lo, smooth=inp["smooth"], topk_idx=inp["topk_idx"])
+        b = time.perf_counter()
+        y = np.ascontiguousarray(inp["x"][lo["src_info"] // c["K"]])  # expert stand-in, not timed
+        e0 = time.perf_counter()
+        oracle.combine(sh, y, inp["topk_idx"], inp["topk_weights"], lo, inp["mask"], inp["ori_x"],
+                       inp["alpha1"], inp["alpha2"], inp["const_v"])
+        dt += (b - a) + (time.perf_counter() - e0)
+        n = lo["num_rows"]
+        total_comm += dispatch_comm_bytes(n, c["H"], c["quant_mode"]) + combine_comm_bytes(n, c["H"])
+        reps += 1
+    return dict(value=round(total_comm / 1e9 / dt, 3), unit="GB/s", cores=1, kind="oracle",
+                sample=f"{reps} whole passes (layout + dispatch + combine) of the timed workload, "
+                       f"{dt:.1f} s single-threaded; oracle combine in float64",
+                seconds_per_pass=round(dt / reps, 4))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--rotate", type=int, default=2, help="input sets cycled through (defeats cache reuse)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, run a plain 512 MiB device copy 3x (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this MoE dispatch/combine path runs on one GPU only; --gpus above 1 is not "
+              "supported (the simulated expert-parallel world of P ranks lives on the one GPU).",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import combine_moe_get_amd as mg
+    from combine_moe_get_amd import workloads
+
+    if not os.path.exists(mg.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cid = args.workload
+    sets = []
+    for r in range(args.rotate):
+        inp = workloads.make_inputs(cid, seed=args.seed + r)
+        sets.append(inp)
+    c = sets[0]["cfg"]
+    T, H, K, E, P, qm = c["T"], c["H"], c["K"], c["E"], c["P"], c["quant_mode"]
+    shape = mg.make_shape(T, H, K, E, P, c["Z"], c["C"], c["Kc"], c["num_max"])
+    cap = T * K
+
+    def d(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    gsets = []
+    for inp in sets:
+        g = dict(topk=d(inp["topk_idx"]), w=d(inp["topk_weights"]), mask=d(inp["mask"]), x=d(inp["x"]),
+                 smooth=d(inp["smooth"]), ori=d(inp["ori_x"]), a1=d(inp["alpha1"]), a2=d(inp["alpha2"]),
+                 v=d(inp["const_v"]))
+        g["lay"] = mg.alloc_layout(shape, dev)
+        g["ws"] = mg.alloc_workspace(shape, dev)
+        g["ex"] = torch.empty((cap, H), dtype=torch.bfloat16 if qm == 0 else torch.int8, device=dev)
+        g["ds"] = torch.empty(cap, dtype=torch.float32, device=dev) if qm == 2 else None
+        g["out"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        # stand-in expert outputs (untimed): dequantized / copied dispatched rows, or N(0,1)
+        mg.layout(shape, g["topk"], g["mask"], out=g["lay"], workspace=g["ws"])
+        mg.dispatch(shape, qm, g["x"], g["lay"].dst_row, g["smooth"], None, g["topk"], g["ex"], g["ds"])
+        torch.cuda.synchronize()
+        n = int(g["lay"].expert_offsets[-1])
+        if c["Kc"] + c["C"] > 0:
+            g["y"] = d(workloads.expert_out_normal(n, H, seed=args.seed, config_id=cid))
+        elif qm == 0:
+            g["y"] = g["ex"][:max(n, 1)].clone()
+        else:
+            y = g["ex"][:max(n, 1)].float() * g["ds"][:max(n, 1), None]
+            if g["smooth"] is not None:
+                y = y / g["smooth"][None, :]
+            g["y"] = y.to(torch.bfloat16).contiguous()
+        g["n"] = n
+        g["n_send"] = int((g["lay"].dst_row >= 0).any(dim=1).sum())
+        ids = g["topk"]
+        special_copy = (ids >= E + c["Z"]) & (ids < E + c["Z"] + c["C"] + c["Kc"])
+        act = torch.ones(T, dtype=torch.bool, device=dev) if g["mask"] is None else g["mask"].bool()
+        g["n_ori"] = int((special_copy.any(dim=1) & act).sum())
+        gsets.append(g)
+    del sets[1:]
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(g, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mg.layout(shape, g["topk"], g["mask"], out=g["lay"], workspace=g["ws"])
+        if ev is not None:
+            ev[1].record(stream)
+        mg.dispatch(shape, qm, g["x"], g["lay"].dst_row, g["smooth"], None, g["topk"], g["ex"], g["ds"])
+        if ev is not None:
+            ev[2].record(stream)
+        mg.combine(shape, g["y"], g["topk"], g["w"], g["lay"].dst_row, g["mask"], g["ori"], g["a1"],
+                   g["a2"], g["v"], out=g["out"])
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(gsets[i % len(gsets)])
+    torch.cuda.synchronize()
+
+    # whole-step timing: K steps between two events, nothing else in between
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(gsets[i % len(gsets)])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+
+    # per-kernel timing: the same steps with events between the calls, on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(gsets[i % len(gsets)], evs[i])
+    torch.cuda.synchronize()
+    lay_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    dis_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    com_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    status = max(int(g["lay"].status[0]) for g in gsets)
+
+    n_avg = float(np.mean([g["n"] for g in gsets]))
+    cb_d = dispatch_comm_bytes(n_avg, H, qm)
+    cb_c = combine_comm_bytes(n_avg, H)
+    hb_d = float(np.mean([dispatch_hbm_bytes(T, H, K, g["n"], g["n_send"], qm, g["smooth"] is not None) for g in gsets]))
+    hb_c = float(np.mean([combine_hbm_bytes(T, H, K, g["n"], g["n_ori"]) for g in gsets]))
+    t_d, t_c, t_l = float(dis_ms.mean()), float(com_ms.mean()), float(lay_ms.mean())
+    us_layer = ms_per_step * 1e3
+    value = (cb_d + cb_c) / 1e9 / (ms_per_step * 1e-3)
+
+    kern = {
+        "dispatch": dict(us=round(t_d * 1e3, 2), us_median=round(float(np.median(dis_ms)) * 1e3, 2),
+                         comm_GBps=round(cb_d / 1e9 / (t_d * 1e-3), 1),
+                         hbm_GBps=round(hb_d / 1e9 / (t_d * 1e-3), 1), hbm_bytes=int(hb_d), comm_bytes=int(cb_d)),
+        "combine": dict(us=round(t_c * 1e3, 2), us_median=round(float(np.median(com_ms)) * 1e3, 2),
+                        comm_GBps=round(cb_c / 1e9 / (t_c * 1e-3), 1),
+                        hbm_GBps=round(hb_c / 1e9 / (t_c * 1e-3), 1), hbm_bytes=int(hb_c), comm_bytes=int(cb_c)),
+        "layout": dict(us=round(t_l * 1e3, 2), us_median=round(float(np.median(lay_ms)) * 1e3, 2), launches=3),
+    }
+    for k in ("dispatch", "combine"):
+        kern[k]["comm_pct_of_peak"] = round(100 * kern[k]["comm_GBps"] / HBM_PEAK_GBPS, 1)
+        kern[k]["hbm_pct_of_peak"] = round(100 * kern[k]["hbm_GBps"] / HBM_PEAK_GBPS, 1)
+    dom = "combine" if t_c >= t_d else "dispatch"
+    ach = kern[dom]["hbm_GBps"]
+    traffic = counter_traffic(dom, c["name"])
+    roofline = dict(bound="hbm", kernel=dom, achieved=ach, peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(ach / HBM_PEAK_GBPS, 4),
+                    traffic=None if traffic is None else int(traffic),
+                    algorithmic_bytes_per_launch=kern[dom]["hbm_bytes"])
+
+    if args.copy_probe:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded generators; no dataset or weights)",
+        "config": {"workload": c["name"], "desc": c["desc"], "T": T, "H": H, "k": K, "E": E, "P": P,
+                   "zero_copy_const": [c["Z"], c["C"], c["Kc"]], "quant_mode": qm,
+                   "num_max_dispatch_tokens_per_rank": c["num_max"], "seed": args.seed,
+                   "rotating_input_sets": len(gsets), "rows_N": n_avg},
+        "us_per_layer": round(us_layer, 2),
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 1),
+        "kernels": kern,
+        "device_status": status,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(sets[0], args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,256 @@
+"""ctypes binding of libmoe_get (include/moe_get.h): argument marshalling only.
+
+Every step runs in the HIP kernels behind the C ABI; this module checks
+tensor dtypes/devices, allocates outputs with PyTorch when the caller does not
+pass them, and hands raw device pointers and the current HIP stream to the
+library.  There is no CPU fallback: without the built library every call
+raises.
+"""
+import ctypes
+import os
+from collections import namedtuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_get.so")
+
+MOE_OK = 0
+QUANT_NONE, QUANT_STATIC_INT8, QUANT_DYNAMIC_INT8 = 0, 1, 2
+DEV_STATUS_BAD_EXPERT_ID = 1
+
+
+class Shape(ctypes.Structure):
+    """moe_get_shape_t."""
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32),
+        ("num_ranks", ctypes.c_int32),
+        ("zero_expert_num", ctypes.c_int32),
+        ("copy_expert_num", ctypes.c_int32),
+        ("const_expert_num", ctypes.c_int32),
+        ("num_max_dispatch_tokens_per_rank", ctypes.c_int32),
+    ]
+
+    @property
+    def n_special(self):
+        return self.zero_expert_num + self.copy_expert_num + self.const_expert_num
+
+    def __repr__(self):
+        return "Shape(" + ", ".join(f"{f}={getattr(self, f)}" for f, _ in self._fields_) + ")"
+
+
+def make_shape(T, H, K, E, P, Z=0, C=0, Kc=0, num_max=0):
+    return Shape(int(T), int(H), int(K), int(E), int(P), int(Z), int(C), int(Kc), int(num_max))
+
+
+class MoeGetError(RuntimeError):
+    def __init__(self, what, status):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build the HIP library first "
+                "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        V, I32, SZ, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_int64
+        SP = ctypes.POINTER(Shape)
+        L.moe_get_abi_version.argtypes = []
+        L.moe_get_abi_version.restype = ctypes.c_int
+        L.moe_get_status_string.argtypes = [ctypes.c_int]
+        L.moe_get_status_string.restype = ctypes.c_char_p
+        L.moe_get_check_shape.argtypes = [SP]
+        L.moe_get_check_shape.restype = ctypes.c_int
+        L.moe_get_recv_capacity.argtypes = [SP]
+        L.moe_get_recv_capacity.restype = I64
+        L.moe_get_workspace_size.argtypes = [SP]
+        L.moe_get_workspace_size.restype = SZ
+        L.moe_get_layout.argtypes = [SP] + [V] * 12 + [V, SZ, V]
+        L.moe_get_layout.restype = ctypes.c_int
+        L.moe_dispatch.argtypes = [SP, I32, V, V, I32, V, V, V, V, V, V, V]
+        L.moe_dispatch.restype = ctypes.c_int
+        L.moe_combine.argtypes = [SP] + [V] * 11
+        L.moe_combine.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().moe_get_status_string(int(status)).decode()
+
+
+def abi_version():
+    return lib().moe_get_abi_version()
+
+
+def check_shape(shape):
+    return lib().moe_get_check_shape(ctypes.byref(shape))
+
+
+def recv_capacity(shape):
+    return lib().moe_get_recv_capacity(ctypes.byref(shape))
+
+
+def workspace_size(shape):
+    return lib().moe_get_workspace_size(ctypes.byref(shape))
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t, name, dtypes, numel=None, required=True):
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device (HIP) tensor, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() > 0 else None
+
+
+BF16 = (torch.bfloat16,)
+I32 = (torch.int32,)
+F32 = (torch.float32,)
+U8 = (torch.uint8, torch.bool)
+
+Layout = namedtuple("Layout", [
+    "num_tokens_per_expert", "expert_offsets", "recv_counts", "special_counts",
+    "num_tokens_per_rank", "rank_offsets", "is_token_in_rank", "dst_row", "src_info", "status",
+])
+
+
+def alloc_layout(shape, device):
+    T, K, E, P = shape.num_tokens, shape.topk, shape.num_experts, shape.num_ranks
+    i32 = dict(dtype=torch.int32, device=device)
+    return Layout(
+        num_tokens_per_expert=torch.empty(E, **i32),
+        expert_offsets=torch.empty(E + 1, **i32),
+        recv_counts=torch.empty((E, P), **i32),
+        special_counts=torch.empty(shape.n_special, **i32),
+        num_tokens_per_rank=torch.empty(P, **i32),
+        rank_offsets=torch.empty(P + 1, **i32),
+        is_token_in_rank=torch.empty((T, P), dtype=torch.uint8, device=device),
+        dst_row=torch.empty((T, K), **i32),
+        src_info=torch.empty(max(T * K, 1), **i32),
+        status=torch.zeros(1, **i32),
+    )
+
+
+def alloc_workspace(shape, device):
+    n = workspace_size(shape)
+    if n == 0:
+        raise MoeGetError("workspace", check_shape(shape))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def layout(shape, topk_idx, x_active_mask=None, out=None, workspace=None, stream=None):
+    """moe_get_layout.  Returns a Layout of device tensors; `status` is a sticky
+    int32 word (bit 1: an out-of-range expert id was dropped)."""
+    st = check_shape(shape)
+    if st != MOE_OK:
+        raise MoeGetError("layout", st)
+    T, K = shape.num_tokens, shape.topk
+    dev = topk_idx.device
+    out = out if out is not None else alloc_layout(shape, dev)
+    workspace = workspace if workspace is not None else alloc_workspace(shape, dev)
+    s = lib().moe_get_layout(
+        ctypes.byref(shape),
+        _ptr(topk_idx, "topk_idx", I32, T * K),
+        _ptr(x_active_mask, "x_active_mask", U8, T, required=False),
+        _ptr(out.num_tokens_per_expert, "num_tokens_per_expert", I32, shape.num_experts),
+        _ptr(out.expert_offsets, "expert_offsets", I32, shape.num_experts + 1),
+        _ptr(out.recv_counts, "recv_counts", I32, shape.num_experts * shape.num_ranks),
+        _ptr(out.special_counts, "special_counts", I32, shape.n_special, required=shape.n_special > 0),
+        _ptr(out.num_tokens_per_rank, "num_tokens_per_rank", I32, shape.num_ranks),
+        _ptr(out.rank_offsets, "rank_offsets", I32, shape.num_ranks + 1),
+        _ptr(out.is_token_in_rank, "is_token_in_rank", U8, T * shape.num_ranks),
+        _ptr(out.dst_row, "dst_row", I32, T * K),
+        _ptr(out.src_info, "src_info", I32, T * K),
+        _ptr(out.status, "status", I32, 1),
+        _ptr(workspace, "workspace", (torch.uint8,)),
+        ctypes.c_size_t(workspace.numel()),
+        _stream(stream),
+    )
+    if s != MOE_OK:
+        raise MoeGetError("moe_get_layout", s)
+    return out
+
+
+def dispatch(shape, quant_mode, x, dst_row, x_smooth_scale=None, topk_weights=None, topk_idx=None,
+             expand_x=None, dynamic_scales=None, expand_weights=None, stream=None):
+    """moe_dispatch.  Returns (expand_x [cap, H], dynamic_scales [cap] or None,
+    expand_weights [cap] or None); rows >= N are left as they were."""
+    T, H, K, E = shape.num_tokens, shape.hidden, shape.topk, shape.num_experts
+    cap = max(T * K, 1)
+    dev = x.device
+    if expand_x is None:
+        expand_x = torch.empty((cap, H), dtype=torch.bfloat16 if quant_mode == 0 else torch.int8, device=dev)
+    if quant_mode == QUANT_DYNAMIC_INT8 and dynamic_scales is None:
+        dynamic_scales = torch.empty(cap, dtype=torch.float32, device=dev)
+    smooth_rows = 0
+    if x_smooth_scale is not None:
+        smooth_rows = 1 if x_smooth_scale.numel() == H else x_smooth_scale.numel() // H
+        if smooth_rows * H != x_smooth_scale.numel() or smooth_rows not in (1, E):
+            raise ValueError("x_smooth_scale must hold [H] or [num_experts, H] floats")
+    s = lib().moe_dispatch(
+        ctypes.byref(shape), int(quant_mode),
+        _ptr(x, "x", BF16, T * H),
+        _ptr(x_smooth_scale, "x_smooth_scale", F32, required=False),
+        smooth_rows,
+        _ptr(topk_weights, "topk_weights", F32, T * K, required=False),
+        _ptr(topk_idx, "topk_idx", I32, T * K, required=False),
+        _ptr(dst_row, "dst_row", I32, T * K),
+        _ptr(expand_x, "expand_x", BF16 if quant_mode == 0 else (torch.int8,)),
+        _ptr(dynamic_scales, "dynamic_scales", F32, required=False),
+        _ptr(expand_weights, "expand_weights", F32, required=False),
+        _stream(stream),
+    )
+    if s != MOE_OK:
+        raise MoeGetError("moe_dispatch", s)
+    return expand_x, dynamic_scales, expand_weights
+
+
+def combine(shape, expert_out, topk_idx, topk_weights, dst_row, x_active_mask=None, ori_x=None,
+            const_alpha1=None, const_alpha2=None, const_v=None, out=None, stream=None):
+    """moe_combine.  Returns out [T, H] bf16."""
+    T, H, K = shape.num_tokens, shape.hidden, shape.topk
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=topk_idx.device)
+    s = lib().moe_combine(
+        ctypes.byref(shape),
+        _ptr(expert_out, "expert_out", BF16),
+        _ptr(topk_idx, "topk_idx", I32, T * K),
+        _ptr(topk_weights, "topk_weights", F32, T * K),
+        _ptr(x_active_mask, "x_active_mask", U8, T, required=False),
+        _ptr(dst_row, "dst_row", I32, T * K),
+        _ptr(ori_x, "ori_x", BF16, T * H, required=False),
+        _ptr(const_alpha1, "const_alpha1", BF16, required=False),
+        _ptr(const_alpha2, "const_alpha2", BF16, required=False),
+        _ptr(const_v, "const_v", BF16, required=False),
+        _ptr(out, "out", BF16, T * H),
+        _stream(stream),
+    )
+    if s != MOE_OK:
+        raise MoeGetError("moe_combine", s)
+    return out

@@ -1,0 +1,225 @@
+// api.hip -- the extern "C" entry points of libmoe_get: argument checks on
+// the host, then kernel launches on the caller's stream.  Nothing here
+// allocates, synchronizes or keeps state.
+//
+// Shape limits come from the Constraints section of the CANN
+// "low_latency_dispatch" page (K, BS, H, local_expert_num * ep_world_size)
+// and its single-operator Example (num_experts a multiple of the rank count,
+// checked before the call); the kernels add H % 8 == 0, H <= 8192 and at most
+// 1024 special ids.
+#include <string.h>
+
+#include "moe_internal.hpp"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int n_special(const moe_get_shape_t *s) {
+  return s->zero_expert_num + s->copy_expert_num + s->const_expert_num;
+}
+
+int check_shape(const moe_get_shape_t *s) {
+  if (!s) return MOE_ERR_ARG;
+  const int T = s->num_tokens, H = s->hidden, K = s->topk, E = s->num_experts, P = s->num_ranks;
+  if (T < 0 || H <= 0 || P <= 0) return MOE_ERR_SHAPE;
+  if (K <= 0 || K > 16) return MOE_ERR_SHAPE;
+  if (E <= 0 || E % P != 0 || E > 2048) return MOE_ERR_SHAPE;
+  if (s->zero_expert_num < 0 || s->copy_expert_num < 0 || s->const_expert_num < 0)
+    return MOE_ERR_SHAPE;
+  const int64_t etot = (int64_t)E + s->zero_expert_num + s->copy_expert_num + s->const_expert_num;
+  if (etot >= INT32_MAX || K > etot) return MOE_ERR_SHAPE;
+  if (T % P != 0) return MOE_ERR_SHAPE;
+  const int BS = T / P;
+  if (BS > 512) return MOE_ERR_SHAPE;
+  if (s->num_max_dispatch_tokens_per_rank < 0) return MOE_ERR_SHAPE;
+  if (s->num_max_dispatch_tokens_per_rank > 0 && BS > s->num_max_dispatch_tokens_per_rank)
+    return MOE_ERR_CAPACITY;
+  if (H % 8 != 0 || H > 8192) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)s->zero_expert_num + s->copy_expert_num + s->const_expert_num > 1024)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// workspace: [P][E] per-chunk expert counts | [P][P] per-chunk rank tokens | [P][NS] per-chunk specials | status word
+struct WsLayout {
+  size_t base, rank_tok, special, status, total;
+};
+
+WsLayout ws_layout(const moe_get_shape_t *s) {
+  const size_t P = s->num_ranks, E = s->num_experts, NS = n_special(s);
+  WsLayout w;
+  w.base = 0;
+  w.rank_tok = w.base + align_up(P * E * 4);
+  w.special = w.rank_tok + align_up(P * P * 4);
+  w.status = w.special + align_up(P * (NS > 0 ? NS : 1) * 4);
+  w.total = w.status + kAlign;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_get_abi_version(void) { return MOE_GET_ABI_VERSION; }
+
+const char *moe_get_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_ARG: return "invalid argument (NULL buffer, misaligned pointer, bad mode or small workspace)";
+    case MOE_ERR_SHAPE: return "shape outside the operator constraints";
+    case MOE_ERR_CAPACITY: return "tokens per rank exceed num_max_dispatch_tokens_per_rank";
+    case MOE_ERR_UNSUPPORTED: return "shape not supported by the kernels (hidden % 8, hidden > 8192 or > 1024 special ids)";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_get_check_shape(const moe_get_shape_t *shape) { return check_shape(shape); }
+
+int64_t moe_get_recv_capacity(const moe_get_shape_t *shape) {
+  if (check_shape(shape) != MOE_OK) return -1;
+  return (int64_t)shape->num_tokens * shape->topk;
+}
+
+size_t moe_get_workspace_size(const moe_get_shape_t *shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return ws_layout(shape).total;
+}
+
+int moe_get_layout(const moe_get_shape_t *shape, const int32_t *topk_idx,
+                   const uint8_t *x_active_mask, int32_t *num_tokens_per_expert,
+                   int32_t *expert_offsets, int32_t *recv_counts, int32_t *special_counts,
+                   int32_t *num_tokens_per_rank, int32_t *rank_offsets,
+                   uint8_t *is_token_in_rank, int32_t *dst_row, int32_t *src_info,
+                   uint32_t *status_dev, void *workspace, size_t workspace_bytes, void *stream) {
+  const int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const int T = shape->num_tokens, K = shape->topk, E = shape->num_experts, P = shape->num_ranks;
+  const int NS = n_special(shape);
+  if (!num_tokens_per_expert || !expert_offsets || !recv_counts || !num_tokens_per_rank ||
+      !rank_offsets)
+    return MOE_ERR_ARG;
+  if (T > 0 && (!topk_idx || !is_token_in_rank || !dst_row || !src_info)) return MOE_ERR_ARG;
+  if (NS > 0 && !special_counts) return MOE_ERR_ARG;
+  const WsLayout w = ws_layout(shape);
+  if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & (kAlign - 1)) != 0)
+    return MOE_ERR_ARG;
+
+  LayoutArgs a;
+  memset(&a, 0, sizeof a);
+  a.topk_idx = topk_idx;
+  a.mask = x_active_mask;
+  a.T = T;
+  a.K = K;
+  a.E = E;
+  a.P = P;
+  a.BS = T / P;
+  a.L = E / P;
+  a.NS = NS;
+  a.nbits = 32 - __builtin_clz((unsigned)E);  // bits of the sentinel key E
+  a.Epad = E + (E & 1);
+  const int S = a.BS * K;
+  a.Spad = S + (S & 1);
+  a.Etot = (int64_t)E + NS;
+  a.cnt = num_tokens_per_expert;
+  a.expert_offsets = expert_offsets;
+  a.recv_counts = recv_counts;
+  a.special_counts = special_counts;
+  a.num_tokens_per_rank = num_tokens_per_rank;
+  a.rank_offsets = rank_offsets;
+  a.dst_row = dst_row;
+  a.src_info = src_info;
+  a.itr = is_token_in_rank;
+  char *ws = (char *)workspace;
+  a.ws_cnt_t = (int32_t *)(ws + w.base);
+  a.ws_rank_tok = (int32_t *)(ws + w.rank_tok);
+  a.ws_special = (int32_t *)(ws + w.special);
+  a.status = status_dev ? status_dev : (uint32_t *)(ws + w.status);
+  return launch_layout(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_dispatch(const moe_get_shape_t *shape, int32_t quant_mode, const uint16_t *x,
+                 const float *x_smooth_scale, int32_t smooth_rows, const float *topk_weights,
+                 const int32_t *topk_idx, const int32_t *dst_row, void *expand_x,
+                 float *dynamic_scales, float *expand_weights, void *stream) {
+  const int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (quant_mode < 0 || quant_mode > 2) return MOE_ERR_ARG;
+  const int T = shape->num_tokens, E = shape->num_experts;
+  bool per_expert = false;
+  const float *smooth = nullptr;
+  if (quant_mode != 0) {
+    if (smooth_rows != 0 && smooth_rows != 1 && smooth_rows != E) return MOE_ERR_ARG;
+    if (smooth_rows > 0) {
+      if (!x_smooth_scale || !aligned16(x_smooth_scale)) return MOE_ERR_ARG;
+      smooth = x_smooth_scale;
+      per_expert = smooth_rows > 1;
+      if (per_expert && !topk_idx) return MOE_ERR_ARG;
+    }
+  }
+  if (T == 0) return MOE_OK;
+  if (!x || !dst_row || !expand_x) return MOE_ERR_ARG;
+  if (!aligned16(x) || !aligned16(expand_x)) return MOE_ERR_ARG;
+
+  DispatchArgs a;
+  a.x = x;
+  a.smooth = smooth;
+  a.w = topk_weights;
+  a.topk_idx = topk_idx;
+  a.dst_row = dst_row;
+  a.expand_x = expand_x;
+  a.dyn_scales = quant_mode == 2 ? dynamic_scales : nullptr;
+  a.expand_w = expand_weights;
+  a.T = T;
+  a.H = shape->hidden;
+  a.K = shape->topk;
+  return launch_dispatch(a, quant_mode, per_expert, (hipStream_t)stream) == hipSuccess ? MOE_OK
+                                                                                      : MOE_ERR_HIP;
+}
+
+int moe_combine(const moe_get_shape_t *shape, const uint16_t *expert_out,
+                const int32_t *topk_idx, const float *topk_weights,
+                const uint8_t *x_active_mask, const int32_t *dst_row, const uint16_t *ori_x,
+                const uint16_t *const_alpha1, const uint16_t *const_alpha2,
+                const uint16_t *const_v, uint16_t *out, void *stream) {
+  const int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const int T = shape->num_tokens;
+  const int C = shape->copy_expert_num, Kc = shape->const_expert_num;
+  if (T == 0) return MOE_OK;
+  if (!expert_out || !topk_idx || !topk_weights || !dst_row || !out) return MOE_ERR_ARG;
+  if (!aligned16(expert_out) || !aligned16(out)) return MOE_ERR_ARG;
+  if (C + Kc > 0 && (!ori_x || !aligned16(ori_x))) return MOE_ERR_ARG;
+  if (Kc > 0 && (!const_alpha1 || !const_alpha2 || !const_v || !aligned16(const_alpha1) ||
+                 !aligned16(const_alpha2) || !aligned16(const_v)))
+    return MOE_ERR_ARG;
+
+  CombineArgs a;
+  a.y = expert_out;
+  a.topk_idx = topk_idx;
+  a.w = topk_weights;
+  a.mask = x_active_mask;
+  a.dst_row = dst_row;
+  a.ori_x = ori_x;
+  a.a1 = const_alpha1;
+  a.a2 = const_alpha2;
+  a.cv = const_v;
+  a.out = out;
+  a.T = T;
+  a.H = shape->hidden;
+  a.K = shape->topk;
+  a.E = shape->num_experts;
+  a.Z = shape->zero_expert_num;
+  a.C = C;
+  a.Kc = Kc;
+  return launch_combine(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // extern "C"

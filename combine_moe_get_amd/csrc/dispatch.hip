@@ -1,0 +1,222 @@
+// dispatch.hip -- quantize (optionally) and scatter the routed copies of each
+// token into its expert-major receive rows.
+//
+// What is computed follows the CANN "low_latency_dispatch" page, Function /
+// Formula, dynamic quantization scenario: quant_out = x (mode 0) or
+// CastToInt8(fp32(x) * scales) (static) or, in the dynamic mode,
+// x_fp32 = fp32(x) * scales, dyn = 127 / max|x_fp32|,
+// q = CastToInt8(x_fp32 * dyn), with 1/dyn sent along with every row.  The
+// alltoallv of quant_out becomes a copy of the row to every receive row the
+// layout gave the token's routed slots.
+//
+// Work split (measured on gfx950: more, smaller waves keep more HBM traffic
+// in flight than one wave per token holding the whole row):
+//  - bf16 copy: one wave per (token, 1 KB slice of the row); lane l loads one
+//    16-byte chunk and stores it to each of the token's K rows.
+//  - int8: one workgroup per token, one lane per 16 channels (32 bytes of
+//    bf16 in, 16 bytes of codes out, so every store instruction of a wave
+//    writes 1 KB contiguous); the dynamic scale needs the row's amax: a wave
+//    max, then a max over the <= 8 waves through LDS.
+// Loads are ordinary (the row is read once, K stores reuse it from VGPRs);
+// stores are non-temporal: receive rows are written once and read by a later
+// kernel.
+#include "moe_internal.hpp"
+
+namespace moe {
+
+__device__ __forceinline__ int sat_code(float p) {
+  float r = __builtin_rintf(p);  // round half to even
+  if (r != r) return 0;          // NaN (0 * inf): code 0
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (int)r;
+}
+
+__device__ __forceinline__ uint32_t pack_i8x4(int a, int b, int c, int d) {
+  return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+         ((uint32_t)(d & 0xff) << 24);
+}
+
+__device__ __forceinline__ void unpack8(const u32x4 &v, float *f) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+// ---- bf16 passthrough --------------------------------------------------------
+// wave gw = (token, slice); slice sl covers 16-byte chunks [64 sl, 64 sl + 64)
+__global__ void __launch_bounds__(256) dispatch_copy_kernel(DispatchArgs a, int nslice) {
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = gw / nslice, sl = gw - t * nslice;
+  if (t >= a.T) return;  // whole wave
+  const int K = a.K, H = a.H, nch = H >> 3;
+
+  int myrow = -1;
+  if (lane < K) myrow = a.dst_row[(size_t)t * K + lane];
+  uint64_t valid = ballot(myrow >= 0);
+  if (valid == 0ull) return;  // masked token, or only special / dropped slots
+  const bool write_w = sl == 0 && myrow >= 0 && a.expand_w;
+
+  const int c = lane + 64 * sl;
+  u32x4 v = u32x4{0u, 0u, 0u, 0u};
+  if (c < nch) v = ((const u32x4 *)(a.x + (size_t)t * H))[c];
+  while (valid) {
+    const int j = __builtin_ctzll(valid);
+    valid &= valid - 1;
+    const int row = readlane(myrow, j);
+    if (c < nch) __builtin_nontemporal_store(v, (u32x4 *)((uint16_t *)a.expand_x + (size_t)row * H) + c);
+  }
+  if (write_w) a.expand_w[myrow] = a.w ? a.w[(size_t)t * K + lane] : 1.0f;
+}
+
+// ---- int8 (static or dynamic) -----------------------------------------------
+// one workgroup per token, blockDim = 64 * ceil(pairs / 64) <= 512; lane p of the
+// block owns channels [16p, 16p + 16) (chunks 2p and 2p + 1)
+template <int MODE, bool PER_EXPERT>
+__global__ void __launch_bounds__(512) dispatch_quant_kernel(DispatchArgs a) {
+  __shared__ float red[8][16];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int t = blockIdx.x;
+  const int K = a.K, H = a.H, nch = H >> 3;
+
+  int myrow = -1;
+  if (lane < K) myrow = a.dst_row[(size_t)t * K + lane];
+  uint64_t valid = ballot(myrow >= 0);
+  if (valid == 0ull) return;  // same for every wave of the block: no barrier is skipped
+  const bool write_w = wv == 0 && myrow >= 0 && a.expand_w;
+
+  const int p = threadIdx.x;
+  const int c0 = 2 * p, c1 = 2 * p + 1;
+  const bool has0 = c0 < nch, has1 = c1 < nch;
+  const int l0 = has0 ? c0 : 0, l1 = has1 ? c1 : 0;  // in-bounds chunks for lanes past the row end
+  const bool wide = (H & 15) == 0;                    // 16-byte code stores stay aligned
+  // every load of the lane is issued before the first use: row chunks, then scales
+  const u32x4 *xr = (const u32x4 *)(a.x + (size_t)t * H);
+  const u32x4 v0 = xr[l0], v1 = xr[l1];
+  f32x4 s4[4] = {f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f},
+                 f32x4{1.f, 1.f, 1.f, 1.f}};
+  auto load_scales = [&](const float *s) {
+    const f32x4 *sp = (const f32x4 *)s;
+    s4[0] = sp[2 * l0];
+    s4[1] = sp[2 * l0 + 1];
+    s4[2] = sp[2 * l1];
+    s4[3] = sp[2 * l1 + 1];
+  };
+  if (!PER_EXPERT && a.smooth) load_scales(a.smooth);
+  float f[16];
+  unpack8(v0, f);
+  unpack8(v1, f + 8);
+
+  // g = fp32(x) * scales, zero on channels past the row end
+  auto scale16 = [&](float *g) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const f32x4 &sv = s4[e >> 2];
+      const float sc = (e & 3) == 0 ? sv.x : (e & 3) == 1 ? sv.y : (e & 3) == 2 ? sv.z : sv.w;
+      g[e] = ((e < 8) ? has0 : has1) ? f[e] * sc : 0.0f;
+    }
+  };
+  auto block_amax = [&](const float *g, int slot) {
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(g[e]));
+    m = wave_max(m);
+    if (lane == 0) red[wv][slot] = m;
+  };
+  auto store_codes = [&](const float *g, float dyn, int row) {
+    int cd[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) cd[e] = sat_code(MODE == 2 ? g[e] * dyn : g[e]);
+    const u32x2 lo = u32x2{pack_i8x4(cd[0], cd[1], cd[2], cd[3]), pack_i8x4(cd[4], cd[5], cd[6], cd[7])};
+    const u32x2 hi = u32x2{pack_i8x4(cd[8], cd[9], cd[10], cd[11]), pack_i8x4(cd[12], cd[13], cd[14], cd[15])};
+    int8_t *dst = (int8_t *)a.expand_x + (size_t)row * H + (size_t)p * 16;
+    if (wide && has1) {
+      __builtin_nontemporal_store((u32x4{lo.x, lo.y, hi.x, hi.y}), (u32x4 *)dst);
+    } else {
+      if (has0) __builtin_nontemporal_store(lo, (u32x2 *)dst);
+      if (has1) __builtin_nontemporal_store(hi, (u32x2 *)(dst + 8));
+    }
+  };
+
+  if constexpr (!PER_EXPERT) {
+    // one code row per token, written to every routed copy
+    float g[16];
+    scale16(g);
+    float dyn = 1.0f;
+    if constexpr (MODE == 2) {
+      block_amax(g, 0);
+      __syncthreads();
+      float amax = red[0][0];
+      for (int w2 = 1; w2 < nw; ++w2) amax = fmaxf(amax, red[w2][0]);
+      dyn = amax > 0.0f ? 127.0f / amax : 0.0f;
+      const float scale = amax > 0.0f ? 1.0f / dyn : 0.0f;
+      if (wv == 0 && myrow >= 0 && a.dyn_scales) a.dyn_scales[myrow] = scale;
+    }
+    while (valid) {
+      const int j = __builtin_ctzll(valid);
+      valid &= valid - 1;
+      store_codes(g, dyn, readlane(myrow, j));
+    }
+  } else {
+    // per-expert smooth scales: each copy is quantized with its expert's row
+    int myid = 0;
+    if (lane < K) myid = a.topk_idx[(size_t)t * K + lane];
+    if constexpr (MODE == 2) {
+      uint64_t m = valid;
+      while (m) {
+        const int j = __builtin_ctzll(m);
+        m &= m - 1;
+        float g[16];
+        load_scales(a.smooth + (size_t)readlane(myid, j) * H);
+        scale16(g);
+        block_amax(g, j);
+      }
+      __syncthreads();
+    }
+    while (valid) {
+      const int j = __builtin_ctzll(valid);
+      valid &= valid - 1;
+      const int row = readlane(myrow, j);
+      float g[16];
+      load_scales(a.smooth + (size_t)readlane(myid, j) * H);
+      scale16(g);
+      float dyn = 1.0f;
+      if constexpr (MODE == 2) {
+        float amax = red[0][j];
+        for (int w2 = 1; w2 < nw; ++w2) amax = fmaxf(amax, red[w2][j]);
+        dyn = amax > 0.0f ? 127.0f / amax : 0.0f;
+        if (threadIdx.x == j && a.dyn_scales) a.dyn_scales[row] = amax > 0.0f ? 1.0f / dyn : 0.0f;
+      }
+      store_codes(g, dyn, row);
+    }
+  }
+  if (write_w) a.expand_w[myrow] = a.w ? a.w[(size_t)t * K + lane] : 1.0f;
+}
+
+hipError_t launch_dispatch(const DispatchArgs &a, int quant_mode, bool per_expert, hipStream_t stream) {
+  if (a.T == 0) return hipSuccess;
+  const int nch = a.H / 8;
+  if (quant_mode == 0) {
+    const int nslice = (nch + 63) / 64;
+    const int64_t waves = (int64_t)a.T * nslice;
+    hipLaunchKernelGGL(dispatch_copy_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a,
+                       nslice);
+    return hipGetLastError();
+  }
+  const int pairs = (nch + 1) / 2;  // <= 512 for H <= 8192
+  const dim3 blk(64 * ((pairs + 63) / 64));
+  const dim3 g((unsigned)a.T);
+  if (quant_mode == 1 && !per_expert)
+    hipLaunchKernelGGL((dispatch_quant_kernel<1, false>), g, blk, 0, stream, a);
+  else if (quant_mode == 1)
+    hipLaunchKernelGGL((dispatch_quant_kernel<1, true>), g, blk, 0, stream, a);
+  else if (!per_expert)
+    hipLaunchKernelGGL((dispatch_quant_kernel<2, false>), g, blk, 0, stream, a);
+  else
+    hipLaunchKernelGGL((dispatch_quant_kernel<2, true>), g, blk, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

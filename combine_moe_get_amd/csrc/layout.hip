@@ -1,0 +1,307 @@
+// layout.hip -- routing layout: counts, offsets, is_token_in_rank, dst_row,
+// src_info for a simulated expert-parallel world (one GPU, P ranks).
+//
+// Rows of expert e are ordered by (source rank, token, slot) (CANN
+// "low_latency_dispatch", Deterministic Computation, read as a stable order);
+// rank r owns experts [rL, rL + L) (DeepEP issue "#84 Questions on Profiling
+// dispatch_t ...", the masking snippet).  Two launches:
+//
+//  1. count (one workgroup per source rank = one chunk of BS tokens): the
+//     chunk's ids are staged in LDS once; per-wave histograms in LDS are built
+//     with a ballot "match" over the expert-id bits, so a wave ranks 64 slots
+//     in order without atomics; a scan over the waves turns them into
+//     chunk-local stable ranks (kept in dst_row), recv_counts[:, s] (and its
+//     transpose in the workspace), is_token_in_rank rows and per-chunk
+//     rank / special counts.
+//  2. scan + finalize (one workgroup per source rank): each reduces the
+//     [P][E] count matrix with all loads in flight at once, scans the expert
+//     totals into offsets and writes dst_row = first row of (s, e) + local
+//     rank and src_info for its chunk; workgroup 0 writes the per-expert and
+//     per-rank outputs.
+//
+// All outputs are fully rewritten on every call; the only atomics are LDS
+// integer adds and an OR into the sticky status word, so results are
+// deterministic.
+#include "moe_internal.hpp"
+
+namespace moe {
+
+int layout_waves(int E) { return E <= 1024 ? 16 : 8; }
+
+size_t layout_lds_bytes(int waves, int Epad, int Spad, int P, int NS, int BS) {
+  return (size_t)Spad * 4 + (size_t)waves * Epad * 2 + (size_t)Spad * 2 + (size_t)P * 4 +
+         (size_t)NS * 4 + (size_t)BS;
+}
+
+__device__ __forceinline__ void zero_bytes(uint8_t *p, size_t n, int tid, int nthr) {
+  const uintptr_t a = (uintptr_t)p;
+  size_t head = (16 - (a & 15)) & 15;
+  if (head > n) head = n;
+  for (size_t i = tid; i < head; i += nthr) p[i] = 0;
+  u32x4 *mid = (u32x4 *)(p + head);
+  const size_t nmid = (n - head) >> 4;
+  for (size_t i = tid; i < nmid; i += nthr) mid[i] = u32x4{0u, 0u, 0u, 0u};
+  for (size_t i = head + (nmid << 4) + tid; i < n; i += nthr) p[i] = 0;
+}
+
+template <int W>
+__global__ void __launch_bounds__(W * 64) layout_count_kernel(LayoutArgs a) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int s = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int K = a.K, E = a.E, P = a.P, BS = a.BS, NS = a.NS;
+  const int S = BS * K;
+  const int t0 = s * BS;
+  const size_t slot0 = (size_t)t0 * K;
+
+  int *ids = (int *)lds;                       // [Spad] the chunk's expert ids
+  uint16_t *cnt = (uint16_t *)(ids + a.Spad);  // [W][Epad] per-wave running counts
+  uint16_t *rk = cnt + W * a.Epad;             // [Spad] rank of a slot inside its wave segment
+  int *rank_tok = (int *)(rk + a.Spad);        // [P]
+  int *spec = rank_tok + P;                    // [NS]
+  uint8_t *act = (uint8_t *)(spec + NS);       // [BS] token active flags
+
+  // one coalesced pass over the chunk's ids and mask; everything after reads LDS
+  for (int i = tid; i < S; i += W * 64) ids[i] = a.topk_idx[slot0 + i];
+  for (int i = tid; i < BS; i += W * 64) act[i] = a.mask ? a.mask[t0 + i] : (uint8_t)1;
+  for (int i = tid; i < W * a.Epad / 2; i += W * 64) ((uint32_t *)cnt)[i] = 0u;
+  for (int i = tid; i < P; i += W * 64) rank_tok[i] = 0;
+  for (int i = tid; i < NS; i += W * 64) spec[i] = 0;
+  zero_bytes(a.itr + (size_t)t0 * P, (size_t)BS * P, tid, W * 64);
+  __syncthreads();
+
+  // ---- token phase: owner ranks, specials, bad ids --------------------------
+  bool bad = false;
+  for (int tl = tid; tl < BS; tl += W * 64) {
+    if (!act[tl]) continue;
+    const int t = t0 + tl;
+    const int *tid_ids = ids + tl * K;
+    int own[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      own[j] = -1;
+      if (j < K) {
+        const int id = tid_ids[j];
+        if (id == -1) {
+        } else if (id < 0 || (int64_t)id >= a.Etot) {
+          bad = true;
+        } else if (id >= E) {
+          atomicAdd(&spec[id - E], 1);
+        } else {
+          own[j] = id / a.L;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j < K && own[j] >= 0) {
+        bool first = true;
+#pragma unroll
+        for (int j2 = 0; j2 < j; ++j2) first = first && (own[j2] != own[j]);
+        if (first) {
+          a.itr[(size_t)t * P + own[j]] = 1;
+          atomicAdd(&rank_tok[own[j]], 1);
+        }
+      }
+    }
+  }
+
+  // ---- ranking phase: wave wv owns slots [beg, end) of the chunk ------------
+  const int seg = (((S + W - 1) / W) + 63) & ~63;
+  const int beg = wv * seg;
+  const int end = min(S, beg + seg);
+  uint16_t *mycnt = cnt + wv * a.Epad;
+  for (int base = beg; base < end; base += 64) {  // uniform per wave
+    const int i = base + lane;
+    int key = E;  // sentinel: not a routed slot
+    if (i < end) {
+      const int id = ids[i];
+      if (act[i / K] && id >= 0 && id < E) key = id;
+    }
+    // lanes holding the same key: AND over the key bits of (ballot or its complement)
+    uint64_t peers = ~0ull;
+    for (int b = 0; b < a.nbits; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t bl = ballot(bit);
+      peers &= bit ? bl : ~bl;
+    }
+    if (key < E) {
+      const int r = (int)mycnt[key] + popc_below(peers);
+      rk[i] = (uint16_t)r;
+      if (((peers >> lane) >> 1) == 0ull) mycnt[key] = (uint16_t)(r + 1);  // last lane of the group
+    }
+  }
+  __syncthreads();
+
+  // ---- exclusive scan over the waves, per expert ----------------------------
+  for (int e = tid; e < E; e += W * 64) {
+    int run = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < W; ++w2) {
+      const int c = cnt[w2 * a.Epad + e];
+      cnt[w2 * a.Epad + e] = (uint16_t)run;
+      run += c;
+    }
+    a.recv_counts[(size_t)e * P + s] = run;
+    a.ws_cnt_t[(size_t)s * E + e] = run;
+  }
+  __syncthreads();
+
+  // ---- chunk-local stable rank of every slot (made global by the next kernel) ---
+  for (int base = beg; base < end; base += 64) {
+    const int i = base + lane;
+    if (i < end) {
+      const int id = ids[i];
+      int v = -1;
+      if (act[i / K] && id >= 0 && id < E) v = (int)mycnt[id] + (int)rk[i];
+      a.dst_row[slot0 + i] = v;
+    }
+  }
+  for (int r = tid; r < P; r += W * 64) a.ws_rank_tok[(size_t)s * P + r] = rank_tok[r];
+  for (int z = tid; z < NS; z += W * 64) a.ws_special[(size_t)s * NS + z] = spec[z];
+  if (bad) atomicOr(a.status, (uint32_t)MOE_DEV_STATUS_BAD_EXPERT_ID);
+}
+
+// Sum of column `col` of a row-major [rows][ld] int matrix over rows r = r0, r0+step, ...,
+// with the part over rows < lim returned separately.  Loads are issued in groups of 8 so the
+// latency is paid once per group, not once per row.
+__device__ __forceinline__ void column_sums(const int32_t *m, int ld, int col, int rows, int r0,
+                                            int step, int lim, int &tot, int &below) {
+  int r = r0;
+  for (; r + 7 * step < rows; r += 8 * step) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = m[(size_t)(r + u * step) * ld + col];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      tot += v[u];
+      below += (r + u * step < lim) ? v[u] : 0;
+    }
+  }
+  for (; r < rows; r += step) {
+    const int v = m[(size_t)r * ld + col];
+    tot += v;
+    below += r < lim ? v : 0;
+  }
+}
+
+// One workgroup of 1024 threads per source rank s.  Every workgroup reduces the [P][E]
+// count matrix (expert totals and the part sent by ranks below s), scans the totals into
+// expert offsets, and turns its own chunk's local ranks into rows; workgroup 0 also
+// writes the per-expert and per-rank outputs.  E <= 2048.
+__global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a) {
+  __shared__ int red_tot[2048];
+  __shared__ int red_pre[2048];
+  __shared__ int totl[2048];
+  __shared__ int basel[2048];
+  __shared__ int offl[2049];
+  __shared__ int wsum[16];
+  const int s = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int E = a.E, P = a.P, NS = a.NS, K = a.K;
+  const int G = E >= 1024 ? 1 : 1024 / E;  // row groups per expert column
+
+  // partial column sums: virtual thread (e, g) sums rows g, g+G, ... of the count matrix
+  for (int v = tid; v < E * G; v += 1024) {
+    const int e = v % E, g = v / E;
+    int tot = 0, below = 0;
+    column_sums(a.ws_cnt_t, E, e, P, g, G, s, tot, below);
+    red_tot[v] = tot;
+    red_pre[v] = below;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) {
+    int tot = 0, below = 0;
+    for (int g = 0; g < G; ++g) {
+      tot += red_tot[g * E + e];
+      below += red_pre[g * E + e];
+    }
+    totl[e] = tot;
+    basel[e] = below;
+  }
+  __syncthreads();
+
+  // exclusive scan of totl[0..E): thread tid owns elements 2tid, 2tid+1
+  const int e0 = 2 * tid, e1 = 2 * tid + 1;
+  const int v0 = e0 < E ? totl[e0] : 0;
+  const int v1 = e1 < E ? totl[e1] : 0;
+  const int local = v0 + v1;
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(incl, o);
+    if (lane >= o) incl += n;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  if (wv == 0) {
+    const int ws = lane < 16 ? wsum[lane] : 0;
+    int wi = ws;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int n = __shfl_up(wi, o);
+      if (lane >= o) wi += n;
+    }
+    if (lane < 16) wsum[lane] = wi - ws;  // exclusive prefix of the wave totals
+  }
+  __syncthreads();
+  const int excl = incl - local + wsum[wv];
+  if (e0 < E) offl[e0] = excl;
+  if (e1 < E) offl[e1] = excl + v0;
+  if (e0 == E - 1 || e1 == E - 1) offl[E] = excl + local;  // the thread holding element E-1 writes N
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) basel[e] += offl[e];
+  __syncthreads();
+
+  // rows of this chunk's slots
+  const int S = a.BS * K;
+  const size_t slot0 = (size_t)s * S;
+  for (int i = tid; i < S; i += 1024) {
+    const int v = a.dst_row[slot0 + i];
+    if (v < 0) continue;
+    const int row = basel[a.topk_idx[slot0 + i]] + v;
+    a.dst_row[slot0 + i] = row;
+    a.src_info[row] = (int)(slot0 + i);
+  }
+
+  if (s != 0) return;
+  for (int e = tid; e < E; e += 1024) {
+    a.cnt[e] = totl[e];
+    a.expert_offsets[e] = offl[e];
+  }
+  if (tid == 0) a.expert_offsets[E] = offl[E];
+  for (int r = tid; r <= P; r += 1024) a.rank_offsets[r] = offl[r * a.L];
+  for (int r = tid; r < P; r += 1024) {
+    int tot = 0, below = 0;
+    column_sums(a.ws_rank_tok, P, r, P, 0, 1, 0, tot, below);
+    a.num_tokens_per_rank[r] = tot;
+  }
+  for (int z = tid; z < NS; z += 1024) {
+    int tot = 0, below = 0;
+    column_sums(a.ws_special, NS, z, P, 0, 1, 0, tot, below);
+    a.special_counts[z] = tot;
+  }
+}
+
+hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {
+  const int W = layout_waves(a.E);
+  const size_t lds = layout_lds_bytes(W, a.Epad, a.Spad, a.P, a.NS, a.BS);
+  // gfx950 has 160 KB of LDS per workgroup; more than 64 KB must be asked for
+  const void *fn = W == 16 ? (const void *)&layout_count_kernel<16> : (const void *)&layout_count_kernel<8>;
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  if (W == 16)
+    hipLaunchKernelGGL(layout_count_kernel<16>, dim3(a.P), dim3(16 * 64), lds, stream, a);
+  else
+    hipLaunchKernelGGL(layout_count_kernel<8>, dim3(a.P), dim3(8 * 64), lds, stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(layout_scan_finalize_kernel, dim3(a.P), dim3(1024), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

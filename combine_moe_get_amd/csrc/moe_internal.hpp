@@ -1,0 +1,103 @@
+// moe_internal.hpp -- device helpers, kernel argument blocks and launcher
+// declarations shared by the HIP translation units of libmoe_get.
+// gfx950 (CDNA4) only: wave64, 16-byte global accesses, LDS for counters.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe_get.h"
+
+namespace moe {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---- wave64 helpers -------------------------------------------------------
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+__device__ __forceinline__ int lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+// number of set bits of m in lanes below the calling lane
+__device__ __forceinline__ int popc_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// wave-wide max through DPP row shifts (device library reduction); exact for any
+// finite values, the result is uniform across the wave
+extern "C" __device__ float __ockl_wfred_max_f32(float);
+__device__ __forceinline__ float wave_max(float v) { return __ockl_wfred_max_f32(v); }
+
+// ---- bf16 <-> fp32 --------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// round to nearest, ties to even (finite values)
+__device__ __forceinline__ uint32_t bf16_rne_hi(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (bf16_rne_hi(lo) >> 16) | bf16_rne_hi(hi);
+}
+
+// ---- kernel argument blocks -----------------------------------------------
+
+struct LayoutArgs {
+  const int32_t *topk_idx;
+  const uint8_t *mask;
+  int32_t T, K, E, P, BS, L, NS, nbits, Epad, Spad;
+  int64_t Etot;
+  int32_t *cnt, *expert_offsets, *recv_counts, *special_counts, *num_tokens_per_rank,
+      *rank_offsets, *dst_row, *src_info;
+  uint8_t *itr;
+  uint32_t *status;
+  int32_t *ws_cnt_t;     // [P][E]  routed copies of expert e sent by rank s
+  int32_t *ws_rank_tok;  // [P][P]  per source rank: tokens with a copy on rank r
+  int32_t *ws_special;   // [P][NS] per source rank: special slots per id
+};
+
+struct DispatchArgs {
+  const uint16_t *x;
+  const float *smooth;
+  const float *w;
+  const int32_t *topk_idx;
+  const int32_t *dst_row;
+  void *expand_x;
+  float *dyn_scales;
+  float *expand_w;
+  int32_t T, H, K;
+};
+
+struct CombineArgs {
+  const uint16_t *y;
+  const int32_t *topk_idx;
+  const float *w;
+  const uint8_t *mask;
+  const int32_t *dst_row;
+  const uint16_t *ori_x, *a1, *a2, *cv;
+  uint16_t *out;
+  int32_t T, H, K, E, Z, C, Kc;
+};
+
+// ---- launchers (return hipSuccess or the launch error) ---------------------
+
+hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream);
+hipError_t launch_dispatch(const DispatchArgs &a, int quant_mode, bool per_expert, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
+
+// LDS bytes of the layout count kernel and its waves per block
+int layout_waves(int E);
+size_t layout_lds_bytes(int waves, int Epad, int Spad, int P, int NS, int BS);
+
+}  // namespace moe

@@ -1,0 +1,83 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/moe_get.h declares, and validates shapes on the host the way the
+Constraints section of the CANN "low_latency_dispatch" page states (checked
+against the oracle's own, independently written, check)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import combine_moe_get_amd as mg
+import oracle
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe_get.h")
+
+
+def _declared_functions():
+    with open(HDR) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("moe_get_layout", "moe_dispatch", "moe_combine", "moe_get_workspace_size",
+              "moe_get_recv_capacity", "moe_get_check_shape"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(mg.LIB_PATH)
+    missing = [n for n in _declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_abi_version_and_status_strings():
+    assert mg.abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5):
+        assert mg.status_string(code) and mg.status_string(code) != "unknown status"
+    assert mg.status_string(42) == "unknown status"
+
+
+SHAPES = [
+    dict(T=4096, H=7168, K=8, E=256, P=32, num_max=128),
+    dict(T=4096, H=7168, K=8, E=256, P=64),
+    dict(T=8192, H=4096, K=8, E=128, P=16, Z=2, C=2, Kc=2),
+    dict(T=16384, H=7168, K=8, E=256, P=64, num_max=256),
+    dict(T=0, H=64, K=4, E=32, P=2),
+    dict(T=8, H=64, K=17, E=32, P=2),
+    dict(T=8, H=64, K=4, E=30, P=4),
+    dict(T=9, H=64, K=4, E=32, P=2),
+    dict(T=1026, H=64, K=4, E=32, P=2),
+    dict(T=8, H=64, K=4, E=4096, P=2),
+    dict(T=8, H=64, K=5, E=4, P=2),
+    dict(T=16, H=64, K=4, E=32, P=2, num_max=4),
+    dict(T=8, H=60, K=4, E=32, P=2),
+    dict(T=8, H=8200, K=4, E=32, P=2),
+    dict(T=8, H=64, K=4, E=32, P=2, Z=600, C=600),
+    dict(T=-8, H=64, K=4, E=32, P=2),
+    dict(T=8, H=64, K=0, E=32, P=2),
+]
+
+
+@pytest.mark.parametrize("kw", SHAPES)
+def test_shape_checks_agree_with_the_oracle(kw):
+    args = (kw["T"], kw["H"], kw["K"], kw["E"], kw["P"], kw.get("Z", 0), kw.get("C", 0),
+            kw.get("Kc", 0), kw.get("num_max", 0))
+    got = mg.check_shape(mg.make_shape(*args))
+    exp = oracle.check_shape(oracle.make_shape(*args))
+    kernel_limit = (kw["H"] % 8 != 0 or kw["H"] > 8192 or
+                    kw.get("Z", 0) + kw.get("C", 0) + kw.get("Kc", 0) > 1024)
+    if exp == 0 and kernel_limit:
+        assert got == -4
+    else:
+        assert got == exp
+
+
+def test_sizes():
+    s = mg.make_shape(4096, 7168, 8, 256, 32, num_max=128)
+    assert mg.recv_capacity(s) == 4096 * 8
+    assert mg.workspace_size(s) >= 4 * (32 * 256 + 32 * 32)
+    assert mg.recv_capacity(mg.make_shape(9, 64, 4, 32, 2)) == -1
+    assert mg.workspace_size(mg.make_shape(9, 64, 4, 32, 2)) == 0
