@@ -1,7 +1,7 @@
 """Benchmark of one MoE layer's data path on one MI355X: routing layout +
 dispatch + combine, timed through the C ABI.
 
-A step is one pass of the whole path over one batch: moe_get_layout (3
+A step is one pass of the whole path over one batch: moe_get_layout (2
 kernels), moe_dispatch (1 kernel), moe_combine (1 kernel), with every input
 already resident in HBM.  The expert computation between dispatch and combine
 is not part of the path; a stand-in expert output (the dequantized dispatched
@@ -231,7 +231,7 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
 
-    # per-kernel timing: the same steps with events between the calls, on the launch stream
+    # per-call timing inside steps: the same steps with events between the calls
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(gsets[i % len(gsets)], evs[i])
@@ -239,6 +239,25 @@ def main():
     lay_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     dis_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     com_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+
+    # kernel durations: each hot kernel launched back to back between two events on its
+    # launch stream (what a kernel trace reports per dispatch)
+    def kernel_avg_ms(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn(gsets[0])
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(args.steps):
+            fn(gsets[i % len(gsets)])
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    k_dis = kernel_avg_ms(lambda g: mg.dispatch(shape, qm, g["x"], g["lay"].dst_row, g["smooth"], None,
+                                                g["topk"], g["ex"], g["ds"]))
+    k_com = kernel_avg_ms(lambda g: mg.combine(shape, g["y"], g["topk"], g["w"], g["lay"].dst_row, g["mask"],
+                                               g["ori"], g["a1"], g["a2"], g["v"], out=g["out"]))
+    k_lay = kernel_avg_ms(lambda g: mg.layout(shape, g["topk"], g["mask"], out=g["lay"], workspace=g["ws"]))
     status = max(int(g["lay"].status[0]) for g in gsets)
 
     n_avg = float(np.mean([g["n"] for g in gsets]))
@@ -246,29 +265,30 @@ def main():
     cb_c = combine_comm_bytes(n_avg, H)
     hb_d = float(np.mean([dispatch_hbm_bytes(T, H, K, g["n"], g["n_send"], qm, g["smooth"] is not None) for g in gsets]))
     hb_c = float(np.mean([combine_hbm_bytes(T, H, K, g["n"], g["n_ori"]) for g in gsets]))
-    t_d, t_c, t_l = float(dis_ms.mean()), float(com_ms.mean()), float(lay_ms.mean())
     us_layer = ms_per_step * 1e3
     value = (cb_d + cb_c) / 1e9 / (ms_per_step * 1e-3)
 
-    kern = {
-        "dispatch": dict(us=round(t_d * 1e3, 2), us_median=round(float(np.median(dis_ms)) * 1e3, 2),
-                         comm_GBps=round(cb_d / 1e9 / (t_d * 1e-3), 1),
-                         hbm_GBps=round(hb_d / 1e9 / (t_d * 1e-3), 1), hbm_bytes=int(hb_d), comm_bytes=int(cb_d)),
-        "combine": dict(us=round(t_c * 1e3, 2), us_median=round(float(np.median(com_ms)) * 1e3, 2),
-                        comm_GBps=round(cb_c / 1e9 / (t_c * 1e-3), 1),
-                        hbm_GBps=round(hb_c / 1e9 / (t_c * 1e-3), 1), hbm_bytes=int(hb_c), comm_bytes=int(cb_c)),
-        "layout": dict(us=round(t_l * 1e3, 2), us_median=round(float(np.median(lay_ms)) * 1e3, 2), launches=3),
-    }
-    for k in ("dispatch", "combine"):
-        kern[k]["comm_pct_of_peak"] = round(100 * kern[k]["comm_GBps"] / HBM_PEAK_GBPS, 1)
-        kern[k]["hbm_pct_of_peak"] = round(100 * kern[k]["hbm_GBps"] / HBM_PEAK_GBPS, 1)
-    dom = "combine" if t_c >= t_d else "dispatch"
+    def kstats(k_ms, call_ms, comm, hbm):
+        d = dict(kernel_us=round(k_ms * 1e3, 2), in_step_us=round(float(call_ms.mean()) * 1e3, 2),
+                 in_step_us_median=round(float(np.median(call_ms)) * 1e3, 2))
+        if comm is not None:
+            d.update(comm_bytes=int(comm), hbm_bytes=int(hbm),
+                     comm_GBps=round(comm / 1e9 / (k_ms * 1e-3), 1), hbm_GBps=round(hbm / 1e9 / (k_ms * 1e-3), 1))
+            d["comm_pct_of_peak"] = round(100 * d["comm_GBps"] / HBM_PEAK_GBPS, 1)
+            d["hbm_pct_of_peak"] = round(100 * d["hbm_GBps"] / HBM_PEAK_GBPS, 1)
+        return d
+
+    kern = {"dispatch": kstats(k_dis, dis_ms, cb_d, hb_d), "combine": kstats(k_com, com_ms, cb_c, hb_c),
+            "layout": kstats(k_lay, lay_ms, None, None)}
+    kern["layout"]["launches"] = 2
+    dom = "combine" if k_com >= k_dis else "dispatch"
     ach = kern[dom]["hbm_GBps"]
     traffic = counter_traffic(dom, c["name"])
     roofline = dict(bound="hbm", kernel=dom, achieved=ach, peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(ach / HBM_PEAK_GBPS, 4),
                     traffic=None if traffic is None else int(traffic),
-                    algorithmic_bytes_per_launch=kern[dom]["hbm_bytes"])
+                    algorithmic_bytes_per_launch=kern[dom]["hbm_bytes"],
+                    kernel_us=kern[dom]["kernel_us"])
 
     if args.copy_probe:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
