@@ -128,6 +128,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=2, help="input sets cycled through (defeats cache reuse)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step per input set in a HIP graph and time graph replays "
+                         "(every replay is checked bit for bit against the eager step)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run a plain 512 MiB device copy 3x (counter calibration)")
     args = ap.parse_args()
@@ -222,11 +225,40 @@ def main():
         step(gsets[i % len(gsets)])
     torch.cuda.synchronize()
 
+    graphs = None
+    if args.graph:
+        # eager reference outputs, then one captured step per input set; every replay below
+        # is compared with the eager result
+        ref = []
+        for g in gsets:
+            step(g)
+            torch.cuda.synchronize()
+            ref.append((g["lay"].dst_row.clone(), g["ex"].clone(), g["out"].clone()))
+        graphs = []
+        for g in gsets:
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                step(g)
+            graphs.append(gr)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            for g, gr, r in zip(gsets, graphs, ref):
+                g["out"].zero_()
+                gr.replay()
+                torch.cuda.synchronize()
+                if not (torch.equal(g["lay"].dst_row, r[0]) and torch.equal(g["ex"], r[1])
+                        and torch.equal(g["out"], r[2])):
+                    raise RuntimeError("graph replay differs from the eager step")
+        stream = torch.cuda.current_stream()
+
     # whole-step timing: K steps between two events, nothing else in between
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
     for i in range(args.steps):
-        step(gsets[i % len(gsets)])
+        if graphs is not None:
+            graphs[i % len(graphs)].replay()
+        else:
+            step(gsets[i % len(gsets)])
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
@@ -313,7 +345,8 @@ def main():
         "config": {"workload": c["name"], "desc": c["desc"], "T": T, "H": H, "k": K, "E": E, "P": P,
                    "zero_copy_const": [c["Z"], c["C"], c["Kc"]], "quant_mode": qm,
                    "num_max_dispatch_tokens_per_rank": c["num_max"], "seed": args.seed,
-                   "rotating_input_sets": len(gsets), "rows_N": n_avg},
+                   "rotating_input_sets": len(gsets), "rows_N": n_avg,
+                   "launch": "hip_graph" if graphs is not None else "eager"},
         "us_per_layer": round(us_layer, 2),
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 1),
         "kernels": kern,
