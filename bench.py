@@ -128,6 +128,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=2, help="input sets cycled through (defeats cache reuse)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rank-stride", default="0",
+                    help="receive layout: 0 compact rows; 'min' or an integer A >= the rank capacity "
+                         "puts rank r's rows in the fixed window [r A, r A + A)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step per input set in a HIP graph and time graph replays "
                          "(every replay is checked bit for bit against the eager step)")
@@ -161,7 +164,8 @@ def main():
     c = sets[0]["cfg"]
     T, H, K, E, P, qm = c["T"], c["H"], c["K"], c["E"], c["P"], c["quant_mode"]
     shape = mg.make_shape(T, H, K, E, P, c["Z"], c["C"], c["Kc"], c["num_max"])
-    cap = T * K
+    A = mg.rank_capacity(shape) if args.rank_stride == "min" else int(args.rank_stride)
+    cap = P * A if A > 0 else T * K
 
     def d(a):
         if a is None:
@@ -176,25 +180,29 @@ def main():
         g = dict(topk=d(inp["topk_idx"]), w=d(inp["topk_weights"]), mask=d(inp["mask"]), x=d(inp["x"]),
                  smooth=d(inp["smooth"]), ori=d(inp["ori_x"]), a1=d(inp["alpha1"]), a2=d(inp["alpha2"]),
                  v=d(inp["const_v"]))
-        g["lay"] = mg.alloc_layout(shape, dev)
+        g["lay"] = mg.alloc_layout(shape, dev, A)
         g["ws"] = mg.alloc_workspace(shape, dev)
         g["ex"] = torch.empty((cap, H), dtype=torch.bfloat16 if qm == 0 else torch.int8, device=dev)
         g["ds"] = torch.empty(cap, dtype=torch.float32, device=dev) if qm == 2 else None
         g["out"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         # stand-in expert outputs (untimed): dequantized / copied dispatched rows, or N(0,1)
-        mg.layout(shape, g["topk"], g["mask"], out=g["lay"], workspace=g["ws"])
+        mg.layout(shape, g["topk"], g["mask"], out=g["lay"], workspace=g["ws"], rank_stride=A)
         mg.dispatch(shape, qm, g["x"], g["lay"].dst_row, g["smooth"], None, g["topk"], g["ex"], g["ds"])
         torch.cuda.synchronize()
         n = int(g["lay"].expert_offsets[-1])
+        used = torch.sort(g["lay"].dst_row[g["lay"].dst_row >= 0]).values.long()  # rows holding a copy
         if c["Kc"] + c["C"] > 0:
-            g["y"] = d(workloads.expert_out_normal(n, H, seed=args.seed, config_id=cid))
+            yv = d(workloads.expert_out_normal(n, H, seed=args.seed, config_id=cid))
         elif qm == 0:
-            g["y"] = g["ex"][:max(n, 1)].clone()
+            yv = g["ex"][used]
         else:
-            y = g["ex"][:max(n, 1)].float() * g["ds"][:max(n, 1), None]
+            yv = g["ex"][used].float() * g["ds"][used, None]
             if g["smooth"] is not None:
-                y = y / g["smooth"][None, :]
-            g["y"] = y.to(torch.bfloat16).contiguous()
+                yv = yv / g["smooth"][None, :]
+            yv = yv.to(torch.bfloat16)
+        g["y"] = torch.empty((max(cap, 1), H), dtype=torch.bfloat16, device=dev)
+        g["y"][used] = yv
+        del yv, used
         g["n"] = n
         g["n_send"] = int((g["lay"].dst_row >= 0).any(dim=1).sum())
         ids = g["topk"]
@@ -210,7 +218,7 @@ def main():
     def step(g, ev=None):
         if ev is not None:
             ev[0].record(stream)
-        mg.layout(shape, g["topk"], g["mask"], out=g["lay"], workspace=g["ws"])
+        mg.layout(shape, g["topk"], g["mask"], out=g["lay"], workspace=g["ws"], rank_stride=A)
         if ev is not None:
             ev[1].record(stream)
         mg.dispatch(shape, qm, g["x"], g["lay"].dst_row, g["smooth"], None, g["topk"], g["ex"], g["ds"])
@@ -289,7 +297,8 @@ def main():
                                                 g["topk"], g["ex"], g["ds"]))
     k_com = kernel_avg_ms(lambda g: mg.combine(shape, g["y"], g["topk"], g["w"], g["lay"].dst_row, g["mask"],
                                                g["ori"], g["a1"], g["a2"], g["v"], out=g["out"]))
-    k_lay = kernel_avg_ms(lambda g: mg.layout(shape, g["topk"], g["mask"], out=g["lay"], workspace=g["ws"]))
+    k_lay = kernel_avg_ms(lambda g: mg.layout(shape, g["topk"], g["mask"], out=g["lay"], workspace=g["ws"],
+                                              rank_stride=A))
     status = max(int(g["lay"].status[0]) for g in gsets)
 
     n_avg = float(np.mean([g["n"] for g in gsets]))
@@ -346,7 +355,8 @@ def main():
                    "zero_copy_const": [c["Z"], c["C"], c["Kc"]], "quant_mode": qm,
                    "num_max_dispatch_tokens_per_rank": c["num_max"], "seed": args.seed,
                    "rotating_input_sets": len(gsets), "rows_N": n_avg,
-                   "launch": "hip_graph" if graphs is not None else "eager"},
+                   "launch": "hip_graph" if graphs is not None else "eager",
+                   "receive_layout": f"rank windows of {A} rows" if A > 0 else "compact"},
         "us_per_layer": round(us_layer, 2),
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 1),
         "kernels": kern,

@@ -7,7 +7,7 @@ behind the C ABI of include/moe_get.h (libmoe_get.so).  This package is the
 thin Python binding over that ABI plus seeded input generators.
 """
 from .binding import (  # noqa: F401
-    DEV_STATUS_BAD_EXPERT_ID, LIB_PATH, QUANT_DYNAMIC_INT8, QUANT_NONE, QUANT_STATIC_INT8,
+    DEV_STATUS_BAD_EXPERT_ID, DEV_STATUS_RANK_OVERFLOW, LIB_PATH, QUANT_DYNAMIC_INT8, QUANT_NONE, QUANT_STATIC_INT8,
     Layout, MoeGetError, Shape, abi_version, alloc_layout, alloc_workspace, check_shape, combine,
-    dispatch, layout, lib, make_shape, recv_capacity, status_string, workspace_size,
+    dispatch, layout, lib, make_shape, rank_capacity, recv_capacity, status_string, workspace_size,
 )

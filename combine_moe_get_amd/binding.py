@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_get.so")
 MOE_OK = 0
 QUANT_NONE, QUANT_STATIC_INT8, QUANT_DYNAMIC_INT8 = 0, 1, 2
 DEV_STATUS_BAD_EXPERT_ID = 1
+DEV_STATUS_RANK_OVERFLOW = 2
 
 
 class Shape(ctypes.Structure):
@@ -78,6 +79,10 @@ def lib():
         L.moe_get_workspace_size.restype = SZ
         L.moe_get_layout.argtypes = [SP] + [V] * 12 + [V, SZ, V]
         L.moe_get_layout.restype = ctypes.c_int
+        L.moe_get_layout_ex.argtypes = [SP, I64] + [V] * 12 + [V, SZ, V]
+        L.moe_get_layout_ex.restype = ctypes.c_int
+        L.moe_get_rank_capacity.argtypes = [SP]
+        L.moe_get_rank_capacity.restype = I64
         L.moe_dispatch.argtypes = [SP, I32, V, V, I32, V, V, V, V, V, V, V]
         L.moe_dispatch.restype = ctypes.c_int
         L.moe_combine.argtypes = [SP] + [V] * 11
@@ -104,6 +109,11 @@ def recv_capacity(shape):
 
 def workspace_size(shape):
     return lib().moe_get_workspace_size(ctypes.byref(shape))
+
+
+def rank_capacity(shape):
+    """Smallest per-rank receive window of the fixed-capacity layout (moe_get_rank_capacity)."""
+    return lib().moe_get_rank_capacity(ctypes.byref(shape))
 
 
 def _stream(stream):
@@ -140,8 +150,9 @@ Layout = namedtuple("Layout", [
 ])
 
 
-def alloc_layout(shape, device):
+def alloc_layout(shape, device, rank_stride=0):
     T, K, E, P = shape.num_tokens, shape.topk, shape.num_experts, shape.num_ranks
+    rows = P * rank_stride if rank_stride > 0 else T * K
     i32 = dict(dtype=torch.int32, device=device)
     return Layout(
         num_tokens_per_expert=torch.empty(E, **i32),
@@ -152,7 +163,7 @@ def alloc_layout(shape, device):
         rank_offsets=torch.empty(P + 1, **i32),
         is_token_in_rank=torch.empty((T, P), dtype=torch.uint8, device=device),
         dst_row=torch.empty((T, K), **i32),
-        src_info=torch.empty(max(T * K, 1), **i32),
+        src_info=torch.empty(max(rows, 1), **i32),
         status=torch.zeros(1, **i32),
     )
 
@@ -164,18 +175,20 @@ def alloc_workspace(shape, device):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def layout(shape, topk_idx, x_active_mask=None, out=None, workspace=None, stream=None):
-    """moe_get_layout.  Returns a Layout of device tensors; `status` is a sticky
-    int32 word (bit 1: an out-of-range expert id was dropped)."""
+def layout(shape, topk_idx, x_active_mask=None, out=None, workspace=None, stream=None, rank_stride=0):
+    """moe_get_layout (rank_stride 0) or moe_get_layout_ex.  Returns a Layout of device
+    tensors; `status` is a sticky int32 word (bit 1: an out-of-range expert id was dropped;
+    bit 2: a copy did not fit its rank window)."""
     st = check_shape(shape)
     if st != MOE_OK:
         raise MoeGetError("layout", st)
     T, K = shape.num_tokens, shape.topk
     dev = topk_idx.device
-    out = out if out is not None else alloc_layout(shape, dev)
+    out = out if out is not None else alloc_layout(shape, dev, rank_stride)
     workspace = workspace if workspace is not None else alloc_workspace(shape, dev)
-    s = lib().moe_get_layout(
-        ctypes.byref(shape),
+    rows = shape.num_ranks * rank_stride if rank_stride > 0 else T * K
+    s = lib().moe_get_layout_ex(
+        ctypes.byref(shape), ctypes.c_int64(int(rank_stride)),
         _ptr(topk_idx, "topk_idx", I32, T * K),
         _ptr(x_active_mask, "x_active_mask", U8, T, required=False),
         _ptr(out.num_tokens_per_expert, "num_tokens_per_expert", I32, shape.num_experts),
@@ -186,7 +199,7 @@ def layout(shape, topk_idx, x_active_mask=None, out=None, workspace=None, stream
         _ptr(out.rank_offsets, "rank_offsets", I32, shape.num_ranks + 1),
         _ptr(out.is_token_in_rank, "is_token_in_rank", U8, T * shape.num_ranks),
         _ptr(out.dst_row, "dst_row", I32, T * K),
-        _ptr(out.src_info, "src_info", I32, T * K),
+        _ptr(out.src_info, "src_info", I32, rows),
         _ptr(out.status, "status", I32, 1),
         _ptr(workspace, "workspace", (torch.uint8,)),
         ctypes.c_size_t(workspace.numel()),
@@ -198,11 +211,13 @@ def layout(shape, topk_idx, x_active_mask=None, out=None, workspace=None, stream
 
 
 def dispatch(shape, quant_mode, x, dst_row, x_smooth_scale=None, topk_weights=None, topk_idx=None,
-             expand_x=None, dynamic_scales=None, expand_weights=None, stream=None):
-    """moe_dispatch.  Returns (expand_x [cap, H], dynamic_scales [cap] or None,
-    expand_weights [cap] or None); rows >= N are left as they were."""
+             expand_x=None, dynamic_scales=None, expand_weights=None, stream=None, rows=None):
+    """moe_dispatch.  Returns (expand_x [rows, H], dynamic_scales [rows] or None,
+    expand_weights [rows] or None); rows not named by dst_row are left as they were.
+    `rows` (default T * K) sizes the outputs allocated here; a fixed-capacity layout
+    needs P * rank_stride."""
     T, H, K, E = shape.num_tokens, shape.hidden, shape.topk, shape.num_experts
-    cap = max(T * K, 1)
+    cap = max(T * K if rows is None else int(rows), 1)
     dev = x.device
     if expand_x is None:
         expand_x = torch.empty((cap, H), dtype=torch.bfloat16 if quant_mode == 0 else torch.int8, device=dev)

@@ -88,6 +88,14 @@ int64_t moe_get_recv_capacity(const moe_get_shape_t *shape) {
   return (int64_t)shape->num_tokens * shape->topk;
 }
 
+int64_t moe_get_rank_capacity(const moe_get_shape_t *shape) {
+  if (check_shape(shape) != MOE_OK) return -1;
+  const int64_t P = shape->num_ranks, BS = shape->num_tokens / shape->num_ranks;
+  const int64_t nm = shape->num_max_dispatch_tokens_per_rank > 0 ? shape->num_max_dispatch_tokens_per_rank : BS;
+  const int64_t L = shape->num_experts / P;
+  return nm * P * (L < shape->topk ? L : shape->topk);
+}
+
 size_t moe_get_workspace_size(const moe_get_shape_t *shape) {
   if (check_shape(shape) != MOE_OK) return 0;
   return ws_layout(shape).total;
@@ -99,8 +107,24 @@ int moe_get_layout(const moe_get_shape_t *shape, const int32_t *topk_idx,
                    int32_t *num_tokens_per_rank, int32_t *rank_offsets,
                    uint8_t *is_token_in_rank, int32_t *dst_row, int32_t *src_info,
                    uint32_t *status_dev, void *workspace, size_t workspace_bytes, void *stream) {
+  return moe_get_layout_ex(shape, 0, topk_idx, x_active_mask, num_tokens_per_expert, expert_offsets,
+                           recv_counts, special_counts, num_tokens_per_rank, rank_offsets,
+                           is_token_in_rank, dst_row, src_info, status_dev, workspace, workspace_bytes,
+                           stream);
+}
+
+int moe_get_layout_ex(const moe_get_shape_t *shape, int64_t rank_stride, const int32_t *topk_idx,
+                      const uint8_t *x_active_mask, int32_t *num_tokens_per_expert,
+                      int32_t *expert_offsets, int32_t *recv_counts, int32_t *special_counts,
+                      int32_t *num_tokens_per_rank, int32_t *rank_offsets,
+                      uint8_t *is_token_in_rank, int32_t *dst_row, int32_t *src_info,
+                      uint32_t *status_dev, void *workspace, size_t workspace_bytes, void *stream) {
   const int st = check_shape(shape);
   if (st != MOE_OK) return st;
+  if (rank_stride < 0) return MOE_ERR_ARG;
+  if (rank_stride > 0 && (rank_stride < moe_get_rank_capacity(shape) ||
+                          rank_stride * shape->num_ranks >= (int64_t)INT32_MAX))
+    return MOE_ERR_CAPACITY;
   const int T = shape->num_tokens, K = shape->topk, E = shape->num_experts, P = shape->num_ranks;
   const int NS = n_special(shape);
   if (!num_tokens_per_expert || !expert_offsets || !recv_counts || !num_tokens_per_rank ||
@@ -128,6 +152,7 @@ int moe_get_layout(const moe_get_shape_t *shape, const int32_t *topk_idx,
   const int S = a.BS * K;
   a.Spad = S + (S & 1);
   a.Etot = (int64_t)E + NS;
+  a.rank_stride = rank_stride;
   a.cnt = num_tokens_per_expert;
   a.expert_offsets = expert_offsets;
   a.recv_counts = recv_counts;

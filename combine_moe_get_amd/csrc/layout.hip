@@ -196,6 +196,7 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
   __shared__ int red_pre[2048];
   __shared__ int totl[2048];
   __shared__ int basel[2048];
+  __shared__ int liml[2048];
   __shared__ int offl[2049];
   __shared__ int wsum[16];
   const int s = blockIdx.x;
@@ -252,19 +253,36 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
   if (e1 < E) offl[e1] = excl + v0;
   if (e0 == E - 1 || e1 == E - 1) offl[E] = excl + local;  // the thread holding element E-1 writes N
   __syncthreads();
-  for (int e = tid; e < E; e += 1024) basel[e] += offl[e];
+  for (int e = tid; e < E; e += 1024) {
+    basel[e] += offl[e];
+    liml[e] = INT32_MAX;
+    if (a.rank_stride > 0) {  // move the owner's rows into its window [r A, r A + A)
+      const int r = e / a.L;
+      const int64_t w0 = (int64_t)r * a.rank_stride;
+      basel[e] = (int)(w0 + basel[e] - offl[r * a.L]);
+      liml[e] = (int)(w0 + a.rank_stride);
+    }
+  }
   __syncthreads();
 
   // rows of this chunk's slots
   const int S = a.BS * K;
   const size_t slot0 = (size_t)s * S;
+  bool overflow = false;
   for (int i = tid; i < S; i += 1024) {
     const int v = a.dst_row[slot0 + i];
     if (v < 0) continue;
-    const int row = basel[a.topk_idx[slot0 + i]] + v;
+    const int e = a.topk_idx[slot0 + i];
+    const int row = basel[e] + v;
+    if (row >= liml[e]) {  // only a token repeating an expert id can overflow its window
+      overflow = true;
+      a.dst_row[slot0 + i] = -1;
+      continue;
+    }
     a.dst_row[slot0 + i] = row;
     a.src_info[row] = (int)(slot0 + i);
   }
+  if (overflow) atomicOr(a.status, (uint32_t)MOE_DEV_STATUS_RANK_OVERFLOW);
 
   if (s != 0) return;
   for (int e = tid; e < E; e += 1024) {

@@ -58,6 +58,7 @@ struct LayoutArgs {
   const uint8_t *mask;
   int32_t T, K, E, P, BS, L, NS, nbits, Epad, Spad;
   int64_t Etot;
+  int64_t rank_stride;  // 0: compact rows; A > 0: rank r owns rows [r A, r A + A)
   int32_t *cnt, *expert_offsets, *recv_counts, *special_counts, *num_tokens_per_rank,
       *rank_offsets, *dst_row, *src_info;
   uint8_t *itr;

@@ -66,7 +66,7 @@ typedef enum moe_get_status {
   MOE_OK = 0,
   MOE_ERR_ARG = -1,         /* NULL where a buffer is required, bad mode, small workspace */
   MOE_ERR_SHAPE = -2,       /* sizes outside the Constraints section */
-  MOE_ERR_CAPACITY = -3,    /* BS > num_max_dispatch_tokens_per_rank */
+  MOE_ERR_CAPACITY = -3,    /* BS > num_max_dispatch_tokens_per_rank, or a rank window below capacity */
   MOE_ERR_UNSUPPORTED = -4, /* allowed by the page but not by these kernels (H % 8, H > 8192, Z+C+Kc > 1024) */
   MOE_ERR_HIP = -5          /* the HIP runtime refused a launch */
 } moe_get_status_t;
@@ -74,6 +74,7 @@ typedef enum moe_get_status {
 /* Bits of the device status word written by moe_get_layout (sticky: the
  * library only ORs bits in; the caller clears the word). */
 #define MOE_DEV_STATUS_BAD_EXPERT_ID 1u /* an id outside [-1, Etot) was seen; its slot was dropped */
+#define MOE_DEV_STATUS_RANK_OVERFLOW 2u /* a copy did not fit its rank's receive window; it was dropped */
 
 /* Quantization modes of dispatch (Formula, dynamic quantization scenario). */
 #define MOE_QUANT_NONE 0          /* expand_x rows are the bf16 tokens, bit for bit */
@@ -93,6 +94,11 @@ int moe_get_check_shape(const moe_get_shape_t *shape);
  * The rows actually used, N, are expert_offsets[E] after moe_get_layout;
  * rows >= N are never written or read. */
 int64_t moe_get_recv_capacity(const moe_get_shape_t *shape);
+
+/* Smallest per-rank receive window A of the fixed-capacity layout: the
+ * Constraints section's A >= num_max * P * min(L, K), with num_max = BS when
+ * num_max_dispatch_tokens_per_rank is 0.  Returns -1 for an invalid shape. */
+int64_t moe_get_rank_capacity(const moe_get_shape_t *shape);
 
 /* Bytes of device workspace moe_get_layout needs (0 for an invalid shape). */
 size_t moe_get_workspace_size(const moe_get_shape_t *shape);
@@ -121,6 +127,30 @@ int moe_get_layout(const moe_get_shape_t *shape, const int32_t *topk_idx,
                    int32_t *num_tokens_per_rank, int32_t *rank_offsets,
                    uint8_t *is_token_in_rank, int32_t *dst_row, int32_t *src_info,
                    uint32_t *status_dev, void *workspace, size_t workspace_bytes, void *stream);
+
+/* moe_get_layout with fixed per-rank receive windows: rank_stride A > 0 puts
+ * the rows rank r receives (in the same stable order) at r*A, r*A + 1, ..., so
+ * every rank owns the window [r*A, (r+1)*A) of a [P * A, H] receive buffer --
+ * the per-rank buffer of capacity A that the Constraints section sizes, and the
+ * layout a transport between ranks needs (one fixed window per destination;
+ * alternate two such buffers between consecutive calls to keep one in flight,
+ * the "two sets of buffers" of the DeepEP issue #84 thread).
+ *  rank_stride   0 (compact rows, exactly moe_get_layout) or
+ *                >= moe_get_rank_capacity(shape), with P * rank_stride < 2^31
+ *                (else MOE_ERR_CAPACITY)
+ *  src_info      [P * rank_stride]; rows of a window past the rank's count are
+ *                left as they were
+ * Counts and offsets (num_tokens_per_expert, expert_offsets, rank_offsets, ...)
+ * describe the routing as in the compact layout; the rows of expert e start at
+ * r*A + expert_offsets[e] - rank_offsets[r] for its owner r.  A copy that would
+ * pass the end of its window (possible only when a token repeats an expert id)
+ * is dropped and MOE_DEV_STATUS_RANK_OVERFLOW is set. */
+int moe_get_layout_ex(const moe_get_shape_t *shape, int64_t rank_stride, const int32_t *topk_idx,
+                      const uint8_t *x_active_mask, int32_t *num_tokens_per_expert,
+                      int32_t *expert_offsets, int32_t *recv_counts, int32_t *special_counts,
+                      int32_t *num_tokens_per_rank, int32_t *rank_offsets,
+                      uint8_t *is_token_in_rank, int32_t *dst_row, int32_t *src_info,
+                      uint32_t *status_dev, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Dispatch: quantize (optionally) and scatter every routed copy of every
  * token into its receive row (the alltoallv of quant_out of the Formula, and

@@ -46,6 +46,10 @@ def lib():
         L.orc_check_shape.restype = ctypes.c_int
         L.orc_layout.argtypes = [P] * 12
         L.orc_layout.restype = ctypes.c_int
+        L.orc_layout_ex.argtypes = [P, ctypes.c_int64] + [P] * 11
+        L.orc_layout_ex.restype = ctypes.c_int
+        L.orc_rank_capacity.argtypes = [P]
+        L.orc_rank_capacity.restype = ctypes.c_int64
         L.orc_quant_token.argtypes = [ctypes.c_int, P, P, P, P]
         L.orc_quant_token.restype = None
         L.orc_quant_static.argtypes = [ctypes.c_int, P, P, P]
@@ -90,11 +94,20 @@ def n_special(shape):
     return shape.zero_expert_num + shape.copy_expert_num + shape.const_expert_num
 
 
-def layout(shape, topk_idx, mask=None):
-    """Routing layout; returns a dict of numpy arrays plus 'status' (1: a bad id was dropped)."""
+def rank_capacity(shape):
+    """Smallest per-rank receive window A of the fixed-capacity layout."""
+    cs = _cs(shape)
+    return lib().orc_rank_capacity(ctypes.byref(cs))
+
+
+def layout(shape, topk_idx, mask=None, rank_stride=0):
+    """Routing layout; returns a dict of numpy arrays plus 'status' (bit 1: a bad id was
+    dropped; bit 2: a copy overflowed its rank window).  rank_stride > 0 places rank r's
+    rows in [r * rank_stride, (r + 1) * rank_stride)."""
     T, K, E, P = shape.num_tokens, shape.topk, shape.num_experts, shape.num_ranks
     topk_idx = _arr(topk_idx, np.int32).reshape(T, K)
     mask = _arr(mask, np.uint8)
+    cap = P * rank_stride if rank_stride > 0 else T * K
     out = dict(
         num_tokens_per_expert=np.zeros(E, np.int32),
         expert_offsets=np.zeros(E + 1, np.int32),
@@ -104,11 +117,11 @@ def layout(shape, topk_idx, mask=None):
         rank_offsets=np.zeros(P + 1, np.int32),
         is_token_in_rank=np.zeros((T, P), np.uint8),
         dst_row=np.full((T, K), -1, np.int32),
-        src_info=np.full(max(T * K, 1), -1, np.int32),
+        src_info=np.full(max(cap, 1), -1, np.int32),
     )
     cs = _cs(shape)
-    st = lib().orc_layout(
-        ctypes.byref(cs), _ptr(topk_idx), _ptr(mask),
+    st = lib().orc_layout_ex(
+        ctypes.byref(cs), int(rank_stride), _ptr(topk_idx), _ptr(mask),
         _ptr(out["num_tokens_per_expert"]), _ptr(out["expert_offsets"]), _ptr(out["recv_counts"]),
         _ptr(out["special_counts"]), _ptr(out["num_tokens_per_rank"]), _ptr(out["rank_offsets"]),
         _ptr(out["is_token_in_rank"]), _ptr(out["dst_row"]), _ptr(out["src_info"]),
@@ -116,7 +129,9 @@ def layout(shape, topk_idx, mask=None):
     out["special_counts"] = out["special_counts"][: n_special(shape)]
     n = int(out["expert_offsets"][E])
     out["num_rows"] = n
-    out["src_info"] = out["src_info"][:n]
+    out["rank_stride"] = int(rank_stride)
+    if rank_stride <= 0:
+        out["src_info"] = out["src_info"][:n]
     out["status"] = st
     return out
 
@@ -144,7 +159,7 @@ def dispatch(shape, quant_mode, x, lay, smooth=None, smooth_rows=None, weights=N
 
     Returns dict(expand_x (uint16 bf16 bits or int8), dynamic_scales, expand_weights)."""
     T, H, K = shape.num_tokens, shape.hidden, shape.topk
-    n = lay["num_rows"]
+    n = lay["num_rows"] if lay.get("rank_stride", 0) <= 0 else shape.num_ranks * lay["rank_stride"]
     x = _arr(x, np.uint16).reshape(T, H)
     smooth = _arr(smooth, np.float32)
     if smooth_rows is None:

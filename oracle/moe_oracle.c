@@ -42,6 +42,9 @@
  *      q = 0 and scale = 0.
  *  R7  combine: out[t] = sum_j w[t,j] * expert_j(x_t), special experts as in
  *      the special expert formulas, evaluated here in double precision.
+ *  R8  the fixed-capacity layout gives rank r the receive window
+ *      [r*A, r*A + A) with A >= num_max * ep_world_size * min(L, K) (the
+ *      Constraints section's A); its rows keep the compact order.
  */
 #include <math.h>
 #include <stdint.h>
@@ -120,6 +123,29 @@ int orc_layout(const orc_shape_t *s, const int32_t *topk_idx, const uint8_t *mas
                int32_t *cnt, int32_t *expert_offsets, int32_t *recv_counts,
                int32_t *special_counts, int32_t *num_tokens_per_rank, int32_t *rank_offsets,
                uint8_t *is_token_in_rank, int32_t *dst_row, int32_t *src_info) {
+  return orc_layout_ex(s, 0, topk_idx, mask, cnt, expert_offsets, recv_counts, special_counts,
+                       num_tokens_per_rank, rank_offsets, is_token_in_rank, dst_row, src_info);
+}
+
+/* Smallest per-rank receive window the Constraints section of [CANN] allows:
+ * A >= num_max * ep_world_size * min(local_expert_num, K), num_max = BS when 0. */
+int64_t orc_rank_capacity(const orc_shape_t *s) {
+  int64_t bs = s->num_ranks > 0 ? s->num_tokens / s->num_ranks : 0;
+  int64_t nm = s->num_max_dispatch_tokens_per_rank > 0 ? s->num_max_dispatch_tokens_per_rank : bs;
+  int64_t L = s->num_ranks > 0 ? s->num_experts / s->num_ranks : 0;
+  int64_t m = L < s->topk ? L : s->topk;
+  return nm * s->num_ranks * m;
+}
+
+/* Layout with fixed per-rank receive windows (rank_stride A > 0): the rows rank r
+ * receives, in the compact order, are placed at r*A, r*A + 1, ...; a row that would
+ * pass r*A + A - 1 (possible only with a repeated expert id in one token) is dropped
+ * (dst_row -1) and the return value gets bit 2.  rank_stride 0 is the compact layout.
+ * Counts and offsets describe the routing in both cases. */
+int orc_layout_ex(const orc_shape_t *s, int64_t rank_stride, const int32_t *topk_idx,
+                  const uint8_t *mask, int32_t *cnt, int32_t *expert_offsets, int32_t *recv_counts,
+                  int32_t *special_counts, int32_t *num_tokens_per_rank, int32_t *rank_offsets,
+                  uint8_t *is_token_in_rank, int32_t *dst_row, int32_t *src_info) {
   const int T = s->num_tokens, K = s->topk, E = s->num_experts, P = s->num_ranks;
   const int L = E / P;
   const int BS = T / P;
@@ -165,10 +191,19 @@ int orc_layout(const orc_shape_t *s, const int32_t *topk_idx, const uint8_t *mas
       for (t = 0; t < T; ++t)
         for (j = 0; j < K; ++j) {
           int32_t id = topk_idx[(size_t)t * K + j];
+          int64_t placed = row;
           if (id != e || slot_class(s, mask, t, id) != SLOT_ROUTED) continue;
-          dst_row[(size_t)t * K + j] = row;
-          src_info[row] = t * K + j;
+          if (rank_stride > 0) {
+            int r = e / L;
+            int64_t local = row - rank_offsets[r];
+            placed = -1;
+            if (local < rank_stride) placed = (int64_t)r * rank_stride + local;
+            else bad |= 2;
+          }
           ++row;
+          if (placed < 0) continue;
+          dst_row[(size_t)t * K + j] = (int32_t)placed;
+          src_info[placed] = t * K + j;
         }
   }
   return bad;

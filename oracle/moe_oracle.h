@@ -35,6 +35,13 @@ int orc_layout(const orc_shape_t *s, const int32_t *topk_idx, const uint8_t *mas
                int32_t *special_counts, int32_t *num_tokens_per_rank, int32_t *rank_offsets,
                uint8_t *is_token_in_rank, int32_t *dst_row, int32_t *src_info);
 
+int64_t orc_rank_capacity(const orc_shape_t *s);
+
+int orc_layout_ex(const orc_shape_t *s, int64_t rank_stride, const int32_t *topk_idx,
+                  const uint8_t *mask, int32_t *cnt, int32_t *expert_offsets, int32_t *recv_counts,
+                  int32_t *special_counts, int32_t *num_tokens_per_rank, int32_t *rank_offsets,
+                  uint8_t *is_token_in_rank, int32_t *dst_row, int32_t *src_info);
+
 void orc_quant_token(int H, const uint16_t *x, const float *scales, int8_t *q, float *scale);
 void orc_quant_static(int H, const uint16_t *x, const float *scales, int8_t *q);
 

@@ -37,11 +37,12 @@ def gpu_layout(shape, topk, mask):
     return lay
 
 
-def layout_to_numpy(lay, n_rows=None):
+def layout_to_numpy(lay, rank_stride=0):
     out = {k: getattr(lay, k).cpu().numpy() for k in lay._fields}
     n = int(out["expert_offsets"][-1])
     out["num_rows"] = n
-    out["src_info"] = out["src_info"][:n]
+    if rank_stride <= 0:
+        out["src_info"] = out["src_info"][:n]
     out["status"] = int(out["status"][0])
     return out
 
@@ -54,7 +55,7 @@ def assert_layout_equal(g, o):
     for k in LAYOUT_KEYS:
         np.testing.assert_array_equal(np.asarray(g[k]).reshape(np.asarray(o[k]).shape), o[k], err_msg=k)
     assert g["num_rows"] == o["num_rows"]
-    assert (g["status"] != 0) == (o["status"] != 0)
+    assert g["status"] == o["status"], (g["status"], o["status"])
 
 
 def assert_combine_close(got_u16, ref, what="combine", match_frac=0.999):
@@ -83,34 +84,45 @@ def smooth_rows_of(smooth, H):
 
 
 def run_case(T, H, K, E, P, Z, C, Kc, topk, mask, x, weights, quant_mode, smooth, Y_fn,
-             ori_x=None, a1=None, a2=None, v=None, num_max=0, label=""):
+             ori_x=None, a1=None, a2=None, v=None, num_max=0, label="", rank_stride=0):
     """Full pipeline on both sides; returns (gpu dict, oracle dict).  Y_fn(oracle_layout,
     oracle_dispatch) builds the expert outputs both combines read."""
     print(f"[case] {label} T={T} H={H} K={K} E={E} P={P} Z={Z} C={C} Kc={Kc} quant={quant_mode} "
-          f"smooth_rows={smooth_rows_of(smooth, H)} mask={'yes' if mask is not None else 'no'}", flush=True)
+          f"smooth_rows={smooth_rows_of(smooth, H)} mask={'yes' if mask is not None else 'no'} "
+          f"rank_stride={rank_stride}", flush=True)
     shape, osh = shapes(T, H, K, E, P, Z, C, Kc, num_max)
-    lo = oracle.layout(osh, topk, mask)
+    lo = oracle.layout(osh, topk, mask, rank_stride=rank_stride)
     do = oracle.dispatch(osh, quant_mode, x, lo, smooth=smooth, weights=weights, topk_idx=topk)
     Y = Y_fn(lo, do)
     co = oracle.combine(osh, Y, topk, weights, lo, mask, ori_x, a1, a2, v)
 
     tk, mk, wd = dev(topk), dev(mask), dev(weights)
-    lay = mg.layout(shape, tk, mk)
-    cap = max(T * K, 1)
+    lay = mg.layout(shape, tk, mk, rank_stride=rank_stride)
+    cap = max(P * rank_stride if rank_stride > 0 else T * K, 1)
     ew = torch.empty(cap, dtype=torch.float32, device=DEV)
-    ex, ds, _ = mg.dispatch(shape, quant_mode, dev(x), lay.dst_row, dev(smooth), wd, tk, expand_weights=ew)
+    ex, ds, _ = mg.dispatch(shape, quant_mode, dev(x), lay.dst_row, dev(smooth), wd, tk, expand_weights=ew,
+                            rows=cap)
     Yd = dev(Y if Y.shape[0] > 0 else np.zeros((1, H), np.uint16))
     out = mg.combine(shape, Yd, tk, wd, lay.dst_row, mk, dev(ori_x), dev(a1), dev(a2), dev(v))
     torch.cuda.synchronize()
-    g = layout_to_numpy(lay)
-    n = g["num_rows"]
-    g["expand_x"] = (host_bf16(ex[:n]) if quant_mode == 0 else ex[:n].cpu().numpy())
-    g["dynamic_scales"] = ds[:n].cpu().numpy() if ds is not None else None
-    g["expand_weights"] = ew[:n].cpu().numpy()
-    g["out"] = host_bf16(out)
+    g = layout_to_numpy(lay, rank_stride)
     o = dict(lo)
     o.update(do)
     o["out"] = co
+    # rows that hold a copy: all of [0, N) in the compact layout, the named rows of each window
+    # in the fixed-capacity layout (the rest of a window is never written)
+    rows = np.sort(lo["dst_row"][lo["dst_row"] >= 0]).astype(np.int64)
+    rt = torch.from_numpy(rows).to(DEV)
+    g["expand_x"] = host_bf16(ex[rt]) if quant_mode == 0 else ex[rt].cpu().numpy()
+    g["dynamic_scales"] = ds[rt].cpu().numpy() if ds is not None else None
+    g["expand_weights"] = ew[rt].cpu().numpy()
+    g["out"] = host_bf16(out)
+    if rank_stride > 0:
+        g["src_info"] = g["src_info"][rows]
+        o["src_info"] = lo["src_info"][rows]
+    o["expand_x"] = do["expand_x"][rows]
+    o["dynamic_scales"] = do["dynamic_scales"][rows]
+    o["expand_weights"] = do["expand_weights"][rows]
     return g, o
 
 

@@ -81,3 +81,10 @@ def test_sizes():
     assert mg.workspace_size(s) >= 4 * (32 * 256 + 32 * 32)
     assert mg.recv_capacity(mg.make_shape(9, 64, 4, 32, 2)) == -1
     assert mg.workspace_size(mg.make_shape(9, 64, 4, 32, 2)) == 0
+
+
+@pytest.mark.parametrize("kw", SHAPES[:5])
+def test_rank_capacity_agrees_with_the_oracle(kw):
+    args = (kw["T"], kw["H"], kw["K"], kw["E"], kw["P"], kw.get("Z", 0), kw.get("C", 0),
+            kw.get("Kc", 0), kw.get("num_max", 0))
+    assert mg.rank_capacity(mg.make_shape(*args)) == oracle.rank_capacity(oracle.make_shape(*args))

@@ -227,3 +227,47 @@ def test_argument_errors_raise_before_launch():
         mg.dispatch(shape, 3, x, lay.dst_row)
     with pytest.raises((TypeError, ValueError)):
         mg.dispatch(shape, 0, x.float(), lay.dst_row)
+
+
+# ---- fixed-capacity (per-rank window) layout -----------------------------------------
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 5])
+def test_rank_window_layout_named_workloads(cid):
+    # layout at full size with rank windows of the minimum capacity A
+    inp = workloads.make_inputs(cid, seed=0)
+    c = inp["cfg"]
+    shape, osh = G.shapes(c["T"], c["H"], c["K"], c["E"], c["P"], c["Z"], c["C"], c["Kc"], c["num_max"])
+    A = mg.rank_capacity(shape)
+    assert A == oracle.rank_capacity(osh)
+    print(f"[case] rank windows, workload {cid}: A={A}", flush=True)
+    lo = oracle.layout(osh, inp["topk_idx"], inp["mask"], rank_stride=A)
+    lay = mg.layout(shape, G.dev(inp["topk_idx"]), G.dev(inp["mask"]), rank_stride=A)
+    torch.cuda.synchronize()
+    g = G.layout_to_numpy(lay, A)
+    rows = np.sort(lo["dst_row"][lo["dst_row"] >= 0])
+    g["src_info"], lo["src_info"] = g["src_info"][rows], lo["src_info"][rows]
+    G.assert_layout_equal(g, lo)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_rank_window_pipeline_fuzz(seed):
+    # whole path on rank windows; repeated ids make some windows overflow (status bit 2)
+    w = workloads.fuzz_world(700 + seed, p_dup=0.3 if seed % 2 else 0.0)
+    r = np.random.default_rng(seed)
+    qm = int(r.integers(0, 3))
+    shape, osh = G.shapes(w["T"], w["H"], w["K"], w["E"], w["P"], w["Z"], w["C"], w["Kc"])
+    A = mg.rank_capacity(shape) + int(r.integers(0, 3))
+    y_fn = lambda lo, do: workloads.expert_out_normal(w["P"] * A, w["H"], seed=seed)
+    g, o = G.run_case(w["T"], w["H"], w["K"], w["E"], w["P"], w["Z"], w["C"], w["Kc"], w["topk_idx"],
+                      w["mask"], w["x"], w["topk_weights"], qm, w["smooth"] if qm else None, y_fn,
+                      w["ori_x"], w["alpha1"], w["alpha2"], w["const_v"], label=f"rank windows {seed}",
+                      rank_stride=A)
+    G.assert_case(g, o, qm)
+
+
+def test_rank_window_below_capacity_is_refused():
+    shape = mg.make_shape(8, 64, 2, 4, 2)
+    tk = torch.zeros((8, 2), dtype=torch.int32, device=G.DEV)
+    with pytest.raises(mg.MoeGetError):
+        mg.layout(shape, tk, rank_stride=mg.rank_capacity(shape) - 1)

@@ -185,3 +185,51 @@ def test_duplicate_ids_take_one_row_per_slot():
 def test_shape_constraints(kw, code):
     sh = oracle.make_shape(kw["T"], kw["H"], kw["K"], kw["E"], kw["P"], num_max=kw.get("num_max", 0))
     assert oracle.check_shape(sh) == code
+
+
+# ---- fixed-capacity (per-rank window) layout -----------------------------------------
+
+
+def test_rank_capacity_closed_form():
+    # the Constraints section: A >= num_max * ep_world_size * min(local_expert_num, K)
+    assert oracle.rank_capacity(oracle.make_shape(4096, 64, 8, 256, 32, num_max=128)) == 128 * 32 * 8
+    assert oracle.rank_capacity(oracle.make_shape(4096, 64, 8, 256, 64)) == 64 * 64 * 4
+    assert oracle.rank_capacity(oracle.make_shape(128, 64, 8, 32, 16, 1, 1, num_max=128)) == 128 * 16 * 2
+
+
+def test_rank_window_hand_case_with_overflow():
+    # P = 2, E = 2 (L = 1), K = 2, one token per rank: A = 1 * 2 * min(1, 2) = 2.  Token 0 lists
+    # expert 0 twice, token 1 lists experts 0 and 1: rank 0 is sent three copies, so the third
+    # (token 1, slot 0) does not fit its window and is dropped.
+    sh = oracle.make_shape(2, 8, 2, 2, 2)
+    assert oracle.rank_capacity(sh) == 2
+    lay = oracle.layout(sh, np.array([[0, 0], [0, 1]], np.int32), rank_stride=2)
+    np.testing.assert_array_equal(lay["dst_row"], [[0, 1], [-1, 2]])
+    np.testing.assert_array_equal(lay["src_info"], [0, 1, 3, -1])
+    assert lay["status"] == 2
+    np.testing.assert_array_equal(lay["num_tokens_per_expert"], [3, 1])  # counts describe the routing
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_rank_window_is_the_compact_layout_shifted(seed):
+    # without repeated ids nothing overflows and every row moves to r*A + (row - rank_offsets[r])
+    r = np.random.default_rng(300 + seed)
+    P = int(r.choice([1, 2, 4, 8]))
+    L = int(r.integers(1, 5))
+    E, K, BS = P * L, int(r.integers(1, min(P * L, 8) + 1)), int(r.integers(1, 30))
+    T = P * BS
+    topk = np.argsort(r.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    topk[r.random((T, K)) < 0.1] = -1
+    sh = oracle.make_shape(T, 16, K, E, P)
+    A = oracle.rank_capacity(sh) + int(r.integers(0, 5))
+    comp = oracle.layout(sh, topk)
+    pad = oracle.layout(sh, topk, rank_stride=A)
+    assert pad["status"] == 0
+    for k in ("num_tokens_per_expert", "expert_offsets", "recv_counts", "num_tokens_per_rank",
+              "rank_offsets", "is_token_in_rank"):
+        np.testing.assert_array_equal(pad[k], comp[k])
+    owner = np.where(topk >= 0, topk // L, 0)
+    exp = np.where(comp["dst_row"] >= 0, owner * A + comp["dst_row"] - comp["rank_offsets"][owner], -1)
+    np.testing.assert_array_equal(pad["dst_row"], exp)
+    valid = exp[exp >= 0]
+    np.testing.assert_array_equal(pad["src_info"][valid], np.flatnonzero(exp.ravel() >= 0))
