@@ -125,6 +125,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--tokens", type=int, default=None, help="override T (a multiple of the rank count)")
+    ap.add_argument("--ranks", type=int, default=None,
+                    help="override P; with --tokens equal to one rank's batch this times one rank's share")
     ap.add_argument("--rotate", type=int, default=2, help="input sets cycled through (defeats cache reuse)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -159,7 +162,7 @@ def main():
     cid = args.workload
     sets = []
     for r in range(args.rotate):
-        inp = workloads.make_inputs(cid, seed=args.seed + r)
+        inp = workloads.make_inputs(cid, seed=args.seed + r, T=args.tokens, P=args.ranks)
         sets.append(inp)
     c = sets[0]["cfg"]
     T, H, K, E, P, qm = c["T"], c["H"], c["K"], c["E"], c["P"], c["quant_mode"]
@@ -214,20 +217,26 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
+    for g in gsets:  # arguments checked and marshalled once; a step is three bare C calls
+        g["c_lay"] = mg.prepare_layout(shape, g["topk"], g["mask"], out=g["lay"], workspace=g["ws"], rank_stride=A)
+        g["c_dis"] = mg.prepare_dispatch(shape, qm, g["x"], g["lay"].dst_row, g["smooth"], None, g["topk"],
+                                         g["ex"], g["ds"], rows=cap)
+        g["c_com"] = mg.prepare_combine(shape, g["y"], g["topk"], g["w"], g["lay"].dst_row, g["mask"], g["ori"],
+                                        g["a1"], g["a2"], g["v"], out=g["out"])
 
-    def step(g, ev=None):
+    def step(g, ev=None, st=None):
+        st = stream if st is None else st
         if ev is not None:
-            ev[0].record(stream)
-        mg.layout(shape, g["topk"], g["mask"], out=g["lay"], workspace=g["ws"], rank_stride=A)
+            ev[0].record(st)
+        g["c_lay"](st)
         if ev is not None:
-            ev[1].record(stream)
-        mg.dispatch(shape, qm, g["x"], g["lay"].dst_row, g["smooth"], None, g["topk"], g["ex"], g["ds"])
+            ev[1].record(st)
+        g["c_dis"](st)
         if ev is not None:
-            ev[2].record(stream)
-        mg.combine(shape, g["y"], g["topk"], g["w"], g["lay"].dst_row, g["mask"], g["ori"], g["a1"],
-                   g["a2"], g["v"], out=g["out"])
+            ev[2].record(st)
+        g["c_com"](st)
         if ev is not None:
-            ev[3].record(stream)
+            ev[3].record(st)
 
     for i in range(args.warmup):
         step(gsets[i % len(gsets)])
@@ -246,7 +255,7 @@ def main():
         for g in gsets:
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr):
-                step(g)
+                step(g, st=torch.cuda.current_stream())
             graphs.append(gr)
         torch.cuda.synchronize()
         for rep in range(3):
@@ -293,12 +302,9 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / args.steps
 
-    k_dis = kernel_avg_ms(lambda g: mg.dispatch(shape, qm, g["x"], g["lay"].dst_row, g["smooth"], None,
-                                                g["topk"], g["ex"], g["ds"]))
-    k_com = kernel_avg_ms(lambda g: mg.combine(shape, g["y"], g["topk"], g["w"], g["lay"].dst_row, g["mask"],
-                                               g["ori"], g["a1"], g["a2"], g["v"], out=g["out"]))
-    k_lay = kernel_avg_ms(lambda g: mg.layout(shape, g["topk"], g["mask"], out=g["lay"], workspace=g["ws"],
-                                              rank_stride=A))
+    k_dis = kernel_avg_ms(lambda g: g["c_dis"](stream))
+    k_com = kernel_avg_ms(lambda g: g["c_com"](stream))
+    k_lay = kernel_avg_ms(lambda g: g["c_lay"](stream))
     status = max(int(g["lay"].status[0]) for g in gsets)
 
     n_avg = float(np.mean([g["n"] for g in gsets]))
@@ -351,7 +357,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded generators; no dataset or weights)",
-        "config": {"workload": c["name"], "desc": c["desc"], "T": T, "H": H, "k": K, "E": E, "P": P,
+        "config": {"workload": c["name"] + ("" if args.tokens is None and args.ranks is None else
+                                            f" (T={T}, P={P} override)"), "desc": c["desc"], "T": T, "H": H, "k": K, "E": E, "P": P,
                    "zero_copy_const": [c["Z"], c["C"], c["Kc"]], "quant_mode": qm,
                    "num_max_dispatch_tokens_per_rank": c["num_max"], "seed": args.seed,
                    "rotating_input_sets": len(gsets), "rows_N": n_avg,

@@ -53,6 +53,25 @@ class MoeGetError(RuntimeError):
         self.status = status
 
 
+class PreparedCall:
+    """One library call with its arguments checked and marshalled once.  Calling it
+    issues the C call on the current (or given) stream with no per-call checks: the
+    tensors it was prepared with must stay alive and keep their shapes."""
+
+    __slots__ = ("_fn", "_args", "_what", "_keep", "result")
+
+    def __init__(self, fn, args, what, keep, result):
+        self._fn, self._args, self._what, self._keep, self.result = fn, list(args), what, keep, result
+
+    def __call__(self, stream=None):
+        s = torch.cuda.current_stream() if stream is None else stream
+        self._args[-1] = ctypes.c_void_p(s.cuda_stream)
+        st = self._fn(*self._args)
+        if st != MOE_OK:
+            raise MoeGetError(self._what, st)
+        return self.result
+
+
 _lib = None
 
 
@@ -175,10 +194,8 @@ def alloc_workspace(shape, device):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def layout(shape, topk_idx, x_active_mask=None, out=None, workspace=None, stream=None, rank_stride=0):
-    """moe_get_layout (rank_stride 0) or moe_get_layout_ex.  Returns a Layout of device
-    tensors; `status` is a sticky int32 word (bit 1: an out-of-range expert id was dropped;
-    bit 2: a copy did not fit its rank window)."""
+def prepare_layout(shape, topk_idx, x_active_mask=None, out=None, workspace=None, rank_stride=0):
+    """Checked, marshalled moe_get_layout_ex call; see layout()."""
     st = check_shape(shape)
     if st != MOE_OK:
         raise MoeGetError("layout", st)
@@ -187,7 +204,7 @@ def layout(shape, topk_idx, x_active_mask=None, out=None, workspace=None, stream
     out = out if out is not None else alloc_layout(shape, dev, rank_stride)
     workspace = workspace if workspace is not None else alloc_workspace(shape, dev)
     rows = shape.num_ranks * rank_stride if rank_stride > 0 else T * K
-    s = lib().moe_get_layout_ex(
+    args = [
         ctypes.byref(shape), ctypes.c_int64(int(rank_stride)),
         _ptr(topk_idx, "topk_idx", I32, T * K),
         _ptr(x_active_mask, "x_active_mask", U8, T, required=False),
@@ -203,19 +220,22 @@ def layout(shape, topk_idx, x_active_mask=None, out=None, workspace=None, stream
         _ptr(out.status, "status", I32, 1),
         _ptr(workspace, "workspace", (torch.uint8,)),
         ctypes.c_size_t(workspace.numel()),
-        _stream(stream),
-    )
-    if s != MOE_OK:
-        raise MoeGetError("moe_get_layout", s)
-    return out
+        None,
+    ]
+    return PreparedCall(lib().moe_get_layout_ex, args, "moe_get_layout",
+                        (shape, topk_idx, x_active_mask, workspace), out)
 
 
-def dispatch(shape, quant_mode, x, dst_row, x_smooth_scale=None, topk_weights=None, topk_idx=None,
-             expand_x=None, dynamic_scales=None, expand_weights=None, stream=None, rows=None):
-    """moe_dispatch.  Returns (expand_x [rows, H], dynamic_scales [rows] or None,
-    expand_weights [rows] or None); rows not named by dst_row are left as they were.
-    `rows` (default T * K) sizes the outputs allocated here; a fixed-capacity layout
-    needs P * rank_stride."""
+def layout(shape, topk_idx, x_active_mask=None, out=None, workspace=None, stream=None, rank_stride=0):
+    """moe_get_layout (rank_stride 0) or moe_get_layout_ex.  Returns a Layout of device
+    tensors; `status` is a sticky int32 word (bit 1: an out-of-range expert id was dropped;
+    bit 2: a copy did not fit its rank window)."""
+    return prepare_layout(shape, topk_idx, x_active_mask, out, workspace, rank_stride)(stream)
+
+
+def prepare_dispatch(shape, quant_mode, x, dst_row, x_smooth_scale=None, topk_weights=None, topk_idx=None,
+                     expand_x=None, dynamic_scales=None, expand_weights=None, rows=None):
+    """Checked, marshalled moe_dispatch call; see dispatch()."""
     T, H, K, E = shape.num_tokens, shape.hidden, shape.topk, shape.num_experts
     cap = max(T * K if rows is None else int(rows), 1)
     dev = x.device
@@ -228,7 +248,7 @@ def dispatch(shape, quant_mode, x, dst_row, x_smooth_scale=None, topk_weights=No
         smooth_rows = 1 if x_smooth_scale.numel() == H else x_smooth_scale.numel() // H
         if smooth_rows * H != x_smooth_scale.numel() or smooth_rows not in (1, E):
             raise ValueError("x_smooth_scale must hold [H] or [num_experts, H] floats")
-    s = lib().moe_dispatch(
+    args = [
         ctypes.byref(shape), int(quant_mode),
         _ptr(x, "x", BF16, T * H),
         _ptr(x_smooth_scale, "x_smooth_scale", F32, required=False),
@@ -239,20 +259,30 @@ def dispatch(shape, quant_mode, x, dst_row, x_smooth_scale=None, topk_weights=No
         _ptr(expand_x, "expand_x", BF16 if quant_mode == 0 else (torch.int8,)),
         _ptr(dynamic_scales, "dynamic_scales", F32, required=False),
         _ptr(expand_weights, "expand_weights", F32, required=False),
-        _stream(stream),
-    )
-    if s != MOE_OK:
-        raise MoeGetError("moe_dispatch", s)
-    return expand_x, dynamic_scales, expand_weights
+        None,
+    ]
+    keep = (shape, x, dst_row, x_smooth_scale, topk_weights, topk_idx)
+    return PreparedCall(lib().moe_dispatch, args, "moe_dispatch", keep,
+                        (expand_x, dynamic_scales, expand_weights))
 
 
-def combine(shape, expert_out, topk_idx, topk_weights, dst_row, x_active_mask=None, ori_x=None,
-            const_alpha1=None, const_alpha2=None, const_v=None, out=None, stream=None):
-    """moe_combine.  Returns out [T, H] bf16."""
+def dispatch(shape, quant_mode, x, dst_row, x_smooth_scale=None, topk_weights=None, topk_idx=None,
+             expand_x=None, dynamic_scales=None, expand_weights=None, stream=None, rows=None):
+    """moe_dispatch.  Returns (expand_x [rows, H], dynamic_scales [rows] or None,
+    expand_weights [rows] or None); rows not named by dst_row are left as they were.
+    `rows` (default T * K) sizes the outputs allocated here; a fixed-capacity layout
+    needs P * rank_stride."""
+    return prepare_dispatch(shape, quant_mode, x, dst_row, x_smooth_scale, topk_weights, topk_idx,
+                            expand_x, dynamic_scales, expand_weights, rows)(stream)
+
+
+def prepare_combine(shape, expert_out, topk_idx, topk_weights, dst_row, x_active_mask=None, ori_x=None,
+                    const_alpha1=None, const_alpha2=None, const_v=None, out=None):
+    """Checked, marshalled moe_combine call; see combine()."""
     T, H, K = shape.num_tokens, shape.hidden, shape.topk
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=topk_idx.device)
-    s = lib().moe_combine(
+    args = [
         ctypes.byref(shape),
         _ptr(expert_out, "expert_out", BF16),
         _ptr(topk_idx, "topk_idx", I32, T * K),
@@ -264,8 +294,15 @@ def combine(shape, expert_out, topk_idx, topk_weights, dst_row, x_active_mask=No
         _ptr(const_alpha2, "const_alpha2", BF16, required=False),
         _ptr(const_v, "const_v", BF16, required=False),
         _ptr(out, "out", BF16, T * H),
-        _stream(stream),
-    )
-    if s != MOE_OK:
-        raise MoeGetError("moe_combine", s)
-    return out
+        None,
+    ]
+    keep = (shape, expert_out, topk_idx, topk_weights, dst_row, x_active_mask, ori_x, const_alpha1,
+            const_alpha2, const_v)
+    return PreparedCall(lib().moe_combine, args, "moe_combine", keep, out)
+
+
+def combine(shape, expert_out, topk_idx, topk_weights, dst_row, x_active_mask=None, ori_x=None,
+            const_alpha1=None, const_alpha2=None, const_v=None, out=None, stream=None):
+    """moe_combine.  Returns out [T, H] bf16."""
+    return prepare_combine(shape, expert_out, topk_idx, topk_weights, dst_row, x_active_mask, ori_x,
+                           const_alpha1, const_alpha2, const_v, out)(stream)

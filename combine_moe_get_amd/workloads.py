@@ -106,10 +106,15 @@ def _grouped(rng, T, E, K, n_groups=8, top_groups=4):
     return idx, _softmax(chosen).astype(np.float32)
 
 
-def make_inputs(config_id, seed=0, with_expert_out=False, T=None):
+def make_inputs(config_id, seed=0, with_expert_out=False, T=None, P=None):
     """Inputs of a named workload.  ``T`` (a multiple of P) may shrink the token
-    count for quick runs; every other size stays as named."""
+    count for quick runs and ``P`` (dividing E) change the simulated rank count;
+    every other size stays as named."""
     c = dict(CONFIGS[config_id])
+    if P is not None:
+        assert c["E"] % P == 0
+        c["P"] = P
+        c["num_max"] = 0
     if T is not None:
         assert T % c["P"] == 0
         c["T"] = T
