@@ -271,3 +271,66 @@ def test_rank_window_below_capacity_is_refused():
     tk = torch.zeros((8, 2), dtype=torch.int32, device=G.DEV)
     with pytest.raises(mg.MoeGetError):
         mg.layout(shape, tk, rank_stride=mg.rank_capacity(shape) - 1)
+
+
+# ---- prepared calls and graph capture ---------------------------------------------------
+
+
+def _prepared_world(cid=2, T=1024, seed=0):
+    inp = workloads.make_inputs(cid, seed=seed, T=T)
+    c = inp["cfg"]
+    shape, osh = G.shapes(c["T"], c["H"], c["K"], c["E"], c["P"], c["Z"], c["C"], c["Kc"], c["num_max"])
+    d = dict(topk=G.dev(inp["topk_idx"]), w=G.dev(inp["topk_weights"]), x=G.dev(inp["x"]),
+             s=G.dev(inp["smooth"]))
+    lay = mg.alloc_layout(shape, G.DEV)
+    ws = mg.alloc_workspace(shape, G.DEV)
+    cap = c["T"] * c["K"]
+    ex = torch.empty((cap, c["H"]), dtype=torch.int8, device=G.DEV)
+    ds = torch.empty(cap, dtype=torch.float32, device=G.DEV)
+    y = G.dev(workloads.expert_out_normal(cap, c["H"], seed=seed))
+    out = torch.empty((c["T"], c["H"]), dtype=torch.bfloat16, device=G.DEV)
+    calls = (mg.prepare_layout(shape, d["topk"], None, out=lay, workspace=ws),
+             mg.prepare_dispatch(shape, 2, d["x"], lay.dst_row, d["s"], None, d["topk"], ex, ds),
+             mg.prepare_combine(shape, y, d["topk"], d["w"], lay.dst_row, out=out))
+    return inp, shape, osh, lay, ex, ds, y, out, calls
+
+
+def test_prepared_calls_match_the_oracle():
+    inp, shape, osh, lay, ex, ds, y, out, calls = _prepared_world()
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    lo = oracle.layout(osh, inp["topk_idx"])
+    do = oracle.dispatch(osh, 2, inp["x"], lo, smooth=inp["smooth"])
+    n = lo["num_rows"]
+    assert np.array_equal(lay.dst_row.cpu().numpy(), lo["dst_row"])
+    assert np.array_equal(ex[:n].cpu().numpy(), do["expand_x"])
+    co = oracle.combine(osh, G.host_bf16(y), inp["topk_idx"], inp["topk_weights"], lo)
+    G.assert_combine_close(G.host_bf16(out), co)
+
+
+def test_graph_replays_match_eager():
+    # the whole path captured once and replayed several times, with eager work and
+    # synchronizations between replays; every replay must equal the eager result bit for bit
+    inp, shape, osh, lay, ex, ds, y, out, calls = _prepared_world(seed=4)
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    ref = (lay.dst_row.clone(), lay.src_info.clone(), ex.clone(), ds.clone(), out.clone())
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        st = torch.cuda.current_stream()
+        for c in calls:
+            c(st)
+    for rep in range(4):
+        out.zero_()
+        lay.dst_row.fill_(-7)
+        ex.zero_()
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        got = (lay.dst_row, lay.src_info, ex, ds, out)
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        calls[2]()  # eager work between replays
+        torch.cuda.synchronize()
