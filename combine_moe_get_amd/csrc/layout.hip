@@ -28,6 +28,11 @@ namespace moe {
 
 int layout_waves(int E) { return E <= 1024 ? 16 : 8; }
 
+// the single-launch layout re-reads every token's ids in each of the P workgroups; that pass is
+// latency-bound, so it only pays while it is short (one launch saved, ~3 us)
+static constexpr int64_t kFusedMaxSlots = 8192;  // measured: faster below ~10K slots, slower above
+static constexpr size_t kMaxLds = 160 * 1024;  // gfx950 LDS per workgroup
+
 size_t layout_lds_bytes(int waves, int Epad, int Spad, int P, int NS, int BS) {
   return (size_t)Spad * 4 + (size_t)waves * Epad * 2 + (size_t)Spad * 2 + (size_t)P * 4 +
          (size_t)NS * 4 + (size_t)BS;
@@ -303,8 +308,251 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
   }
 }
 
+
+// ---- single-launch layout ---------------------------------------------------
+// One workgroup per source rank s, no communication between workgroups: each
+// first histograms the ids of ALL tokens (token-parallel, LDS integer atomics --
+// counts do not depend on order), split into tokens of ranks below s (hist_lo)
+// and the rest (hist_hi).  Expert totals are hist_lo + hist_hi, the first row of
+// (s, e) is offset[e] + hist_lo[e]; the chunk's own slots are then ranked in order
+// with the ballot match and written as final rows.  Workgroup 0 also writes the
+// per-expert / per-rank outputs (it saw every token).  Used while the redundant
+// pass stays small (T * K bounded); larger worlds take the two-launch path.
+template <int W>
+__global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  __shared__ int wsum[16];
+  constexpr int NT = W * 64;
+  const int s = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int T = a.T, K = a.K, E = a.E, P = a.P, BS = a.BS, NS = a.NS;
+  const int Etot = E + NS;
+  const int Ep2 = (Etot + 1) & ~1;
+  const int S = BS * K;
+  const int t0 = s * BS;
+  const size_t slot0 = (size_t)t0 * K;
+
+  int *hist_lo = (int *)lds;                     // [Ep2] ids of tokens of ranks < s
+  int *hist_hi = hist_lo + Ep2;                  // [Ep2] ids of tokens of ranks >= s
+  int *rtok = hist_hi + Ep2;                     // [P]  distinct tokens per rank (block 0)
+  int *offl = rtok + P;                          // [E + 1]
+  int *basel = offl + E + 1;                     // [E]
+  int *liml = basel + E;                         // [E]
+  int *ids = liml + E;                           // [Spad]
+  uint16_t *cnt = (uint16_t *)(ids + a.Spad);    // [W][Epad]
+  uint16_t *rk = cnt + W * a.Epad;               // [Spad]
+  uint8_t *act = (uint8_t *)(rk + a.Spad);       // [BS]
+
+  for (int i = tid; i < 2 * Ep2; i += NT) hist_lo[i] = 0;
+  for (int i = tid; i < P; i += NT) rtok[i] = 0;
+  for (int i = tid; i < W * a.Epad / 2; i += NT) ((uint32_t *)cnt)[i] = 0u;
+  for (int i = tid; i < S; i += NT) ids[i] = a.topk_idx[slot0 + i];
+  for (int i = tid; i < BS; i += NT) act[i] = a.mask ? a.mask[t0 + i] : (uint8_t)1;
+  zero_bytes(a.itr + (size_t)t0 * P, (size_t)BS * P, tid, NT);
+  __syncthreads();
+
+  // ---- every token's ids: totals, counts below this rank, distinct tokens per rank ----
+  bool bad = false;
+  const bool vec4 = (K & 3) == 0 && (((uintptr_t)a.topk_idx) & 15) == 0;
+  for (int t = tid; t < T; t += NT) {
+    if (a.mask && !a.mask[t]) continue;
+    int *h = t < t0 ? hist_lo : hist_hi;
+    const int32_t *tk = a.topk_idx + (size_t)t * K;
+    int idv[16];
+    if (vec4) {  // a token's K ids as 16-byte loads
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (4 * q < K) {
+          const int4 v = ((const int4 *)tk)[q];
+          idv[4 * q] = v.x; idv[4 * q + 1] = v.y; idv[4 * q + 2] = v.z; idv[4 * q + 3] = v.w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j < K) idv[j] = tk[j];
+    }
+    int own[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      own[j] = -1;
+      if (j < K) {
+        const int id = idv[j];
+        if (id == -1) {
+        } else if (id < 0 || id >= Etot) {
+          bad = true;
+        } else {
+          atomicAdd(&h[id], 1);
+          if (s == 0 && id < E) own[j] = id / a.L;
+        }
+      }
+    }
+    if (s == 0) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (j < K && own[j] >= 0) {
+          bool first = true;
+#pragma unroll
+          for (int j2 = 0; j2 < j; ++j2) first = first && (own[j2] != own[j]);
+          if (first) atomicAdd(&rtok[own[j]], 1);
+        }
+      }
+    }
+  }
+
+  // ---- this chunk: is_token_in_rank rows -------------------------------------
+  for (int tl = tid; tl < BS; tl += NT) {
+    if (!act[tl]) continue;
+    const int *ti = ids + tl * K;
+    for (int j = 0; j < K; ++j) {
+      const int id = ti[j];
+      if (id >= 0 && id < E) a.itr[(size_t)(t0 + tl) * P + id / a.L] = 1;
+    }
+  }
+
+  // ---- this chunk: stable ranks inside each wave segment (ballot match) -------
+  const int seg = (((S + W - 1) / W) + 63) & ~63;
+  const int beg = wv * seg;
+  const int end = min(S, beg + seg);
+  uint16_t *mycnt = cnt + wv * a.Epad;
+  for (int base = beg; base < end; base += 64) {
+    const int i = base + lane;
+    int key = E;
+    if (i < end) {
+      const int id = ids[i];
+      if (act[i / K] && id >= 0 && id < E) key = id;
+    }
+    uint64_t peers = ~0ull;
+    for (int b = 0; b < a.nbits; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t bl = ballot(bit);
+      peers &= bit ? bl : ~bl;
+    }
+    if (key < E) {
+      const int r = (int)mycnt[key] + popc_below(peers);
+      rk[i] = (uint16_t)r;
+      if (((peers >> lane) >> 1) == 0ull) mycnt[key] = (uint16_t)(r + 1);
+    }
+  }
+  __syncthreads();
+
+  // ---- per expert: scan over the waves (chunk-local bases), recv_counts column ---
+  for (int e = tid; e < E; e += NT) {
+    int run = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < W; ++w2) {
+      const int c = cnt[w2 * a.Epad + e];
+      cnt[w2 * a.Epad + e] = (uint16_t)run;
+      run += c;
+    }
+    a.recv_counts[(size_t)e * P + s] = run;
+  }
+
+  // ---- expert offsets: exclusive scan of the totals (each thread 2 * ceil(E / 2NT) experts) ---
+  {
+    constexpr int PER = 4;  // E <= 2048 with W >= 8: at most 4 experts per thread
+    int v[PER], local = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid * PER + u;
+      v[u] = e < E ? hist_lo[e] + hist_hi[e] : 0;
+      local += v[u];
+    }
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int n = __shfl_up(incl, o);
+      if (lane >= o) incl += n;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    if (wv == 0) {
+      const int ws = lane < W ? wsum[lane] : 0;
+      int wi = ws;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const int n = __shfl_up(wi, o);
+        if (lane >= o) wi += n;
+      }
+      if (lane < W) wsum[lane] = wi - ws;
+    }
+    __syncthreads();
+    int run = incl - local + wsum[wv];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid * PER + u;
+      if (e < E) offl[e] = run;
+      run += v[u];
+      if (e == E - 1) offl[E] = run;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += NT) {
+    basel[e] = offl[e] + hist_lo[e];
+    liml[e] = INT32_MAX;
+    if (a.rank_stride > 0) {  // rank r's rows go to its window [r A, r A + A)
+      const int r = e / a.L;
+      const int64_t w0 = (int64_t)r * a.rank_stride;
+      basel[e] = (int)(w0 + basel[e] - offl[r * a.L]);
+      liml[e] = (int)(w0 + a.rank_stride);
+    }
+  }
+  __syncthreads();
+
+  // ---- rows of this chunk ---------------------------------------------------------
+  bool overflow = false;
+  for (int base = beg; base < end; base += 64) {
+    const int i = base + lane;
+    if (i >= end) continue;
+    const int id = ids[i];
+    int row = -1;
+    if (act[i / K] && id >= 0 && id < E) {
+      row = basel[id] + (int)mycnt[id] + (int)rk[i];
+      if (row >= liml[id]) {  // only a token repeating an expert id can overflow its window
+        overflow = true;
+        row = -1;
+      } else {
+        a.src_info[row] = (int)(slot0 + i);
+      }
+    }
+    a.dst_row[slot0 + i] = row;
+  }
+  if (overflow) atomicOr(a.status, (uint32_t)MOE_DEV_STATUS_RANK_OVERFLOW);
+
+  if (s != 0) return;
+  if (bad) atomicOr(a.status, (uint32_t)MOE_DEV_STATUS_BAD_EXPERT_ID);
+  for (int e = tid; e < E; e += NT) {
+    a.cnt[e] = offl[e + 1] - offl[e];
+    a.expert_offsets[e] = offl[e];
+  }
+  if (tid == 0) a.expert_offsets[E] = offl[E];
+  for (int r = tid; r <= P; r += NT) a.rank_offsets[r] = offl[r * a.L];
+  for (int r = tid; r < P; r += NT) a.num_tokens_per_rank[r] = rtok[r];
+  for (int z = tid; z < NS; z += NT) a.special_counts[z] = hist_lo[E + z] + hist_hi[E + z];
+}
+
+size_t layout_fused_lds_bytes(int waves, int E, int NS, int Epad, int Spad, int P, int BS) {
+  const size_t ep2 = (size_t)((E + NS + 1) & ~1);
+  return 2 * ep2 * 4 + (size_t)P * 4 + (size_t)(E + 1) * 4 + 2 * (size_t)E * 4 + (size_t)Spad * 4 +
+         (size_t)waves * Epad * 2 + (size_t)Spad * 2 + (size_t)BS;
+}
+
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {
   const int W = layout_waves(a.E);
+  // single launch while each workgroup's pass over every token stays small
+  const size_t flds = layout_fused_lds_bytes(W, a.E, a.NS, a.Epad, a.Spad, a.P, a.BS);
+  if ((int64_t)a.T * a.K <= kFusedMaxSlots && flds <= kMaxLds) {
+    const void *fn = W == 16 ? (const void *)&layout_fused_kernel<16> : (const void *)&layout_fused_kernel<8>;
+    if (flds > 65536) {
+      const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)flds);
+      if (e != hipSuccess) return e;
+    }
+    if (W == 16)
+      hipLaunchKernelGGL(layout_fused_kernel<16>, dim3(a.P), dim3(16 * 64), flds, stream, a);
+    else
+      hipLaunchKernelGGL(layout_fused_kernel<8>, dim3(a.P), dim3(8 * 64), flds, stream, a);
+    return hipGetLastError();
+  }
   const size_t lds = layout_lds_bytes(W, a.Epad, a.Spad, a.P, a.NS, a.BS);
   // gfx950 has 160 KB of LDS per workgroup; more than 64 KB must be asked for
   const void *fn = W == 16 ? (const void *)&layout_count_kernel<16> : (const void *)&layout_count_kernel<8>;

@@ -334,3 +334,26 @@ def test_graph_replays_match_eager():
             assert torch.equal(a, b), f"replay {rep} differs"
         calls[2]()  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("stride", [0, -1])
+def test_two_launch_layout_for_large_worlds(stride):
+    # T * K above the single-launch bound (8192 slots) takes the two-launch layout, the small
+    # worlds of the other tests the single-launch one; both must agree with the oracle
+    P, BS, K, E, H = 64, 512, 16, 256, 64
+    T = P * BS
+    r = np.random.default_rng(12)
+    topk = np.argsort(r.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    topk[r.random((T, K)) < 0.05] = -1
+    mask = (r.random(T) < 0.95).astype(np.uint8)
+    shape, osh = G.shapes(T, H, K, E, P)
+    A = mg.rank_capacity(shape) if stride else 0
+    print(f"[case] two-launch layout T={T} K={K} A={A}", flush=True)
+    lo = oracle.layout(osh, topk, mask, rank_stride=A)
+    lay = mg.layout(shape, G.dev(topk), G.dev(mask), rank_stride=A)
+    torch.cuda.synchronize()
+    g = G.layout_to_numpy(lay, A)
+    if A:
+        rows = np.sort(lo["dst_row"][lo["dst_row"] >= 0])
+        g["src_info"], lo["src_info"] = g["src_info"][rows], lo["src_info"][rows]
+    G.assert_layout_equal(g, lo)
