@@ -50,10 +50,10 @@ def combine_comm_bytes(n_rows, hidden):
     return comm_bytes(n_rows, hidden, 2, 0)
 
 
-def dispatch_hbm_bytes(T, H, K, n_rows, n_tok_sending, quant_mode, smooth):
+def dispatch_hbm_bytes(T, H, K, n_rows, n_tok_sending, quant_mode, smooth_rows):
     """Algorithmic HBM bytes of one dispatch launch: each sending token's row is read once,
-    every routed copy written once, plus the slot map and the per-row scale."""
-    rd = n_tok_sending * 2 * H + T * K * 4 + (4 * H if smooth else 0)
+    every routed copy written once, plus the slot map, the smooth scales and the per-row scale."""
+    rd = n_tok_sending * 2 * H + T * K * 4 + 4 * H * int(smooth_rows)
     wr = n_rows * (H * (2 if quant_mode == 0 else 1) + (4 if quant_mode == 2 else 0))
     return rd + wr
 
@@ -300,6 +300,9 @@ def main():
     ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--tokens", type=int, default=None, help="override T (a multiple of the rank count)")
+    ap.add_argument("--quant", type=int, default=None, choices=[0, 1, 2], help="override the quant mode")
+    ap.add_argument("--smooth", default=None, choices=["none", "channel", "expert"],
+                    help="override the smooth scales: none, one [H] vector, or [E, H] per expert")
     ap.add_argument("--ranks", type=int, default=None,
                     help="override P; with --tokens equal to one rank's batch this times one rank's share")
     ap.add_argument("--rotate", type=int, default=2, help="input sets cycled through (defeats cache reuse)")
@@ -349,6 +352,14 @@ def main():
         sets.append(inp)
     c = sets[0]["cfg"]
     T, H, K, E, P, qm = c["T"], c["H"], c["K"], c["E"], c["P"], c["quant_mode"]
+    if args.quant is not None:
+        qm = c["quant_mode"] = args.quant
+    if args.smooth is not None:
+        for r, inp in enumerate(sets):
+            rng = workloads.rng_for(args.seed + r, cid, 4)
+            inp["smooth"] = (None if args.smooth == "none" else
+                             rng.uniform(0.5, 1.5, H if args.smooth == "channel" else (E, H)).astype(np.float32))
+        c["smooth"] = args.smooth
     shape = mg.make_shape(T, H, K, E, P, c["Z"], c["C"], c["Kc"], c["num_max"])
     A = mg.rank_capacity(shape) if args.rank_stride == "min" else int(args.rank_stride)
     cap = P * A if A > 0 else T * K
@@ -377,7 +388,7 @@ def main():
         torch.cuda.synchronize()
         n = int(g["lay"].expert_offsets[-1])
         used = torch.sort(g["lay"].dst_row[g["lay"].dst_row >= 0]).values.long()  # rows holding a copy
-        if c["Kc"] + c["C"] > 0:
+        if c["Kc"] + c["C"] > 0 or qm == 1 or (g["smooth"] is not None and g["smooth"].dim() == 2):
             yv = d(workloads.expert_out_normal(n, H, seed=args.seed, config_id=cid))
         elif qm == 0:
             yv = g["ex"][used]
@@ -493,7 +504,9 @@ def main():
     n_avg = float(np.mean([g["n"] for g in gsets]))
     cb_d = dispatch_comm_bytes(n_avg, H, qm)
     cb_c = combine_comm_bytes(n_avg, H)
-    hb_d = float(np.mean([dispatch_hbm_bytes(T, H, K, g["n"], g["n_send"], qm, g["smooth"] is not None) for g in gsets]))
+    hb_d = float(np.mean([dispatch_hbm_bytes(T, H, K, g["n"], g["n_send"], qm,
+                                             0 if g["smooth"] is None else g["smooth"].numel() // H)
+                          for g in gsets]))
     hb_c = float(np.mean([combine_hbm_bytes(T, H, K, g["n"], g["n_ori"]) for g in gsets]))
     us_layer = ms_per_step * 1e3
     value = (cb_d + cb_c) / 1e9 / (ms_per_step * 1e-3)
@@ -543,6 +556,8 @@ def main():
         "config": {"workload": c["name"] + ("" if args.tokens is None and args.ranks is None else
                                             f" (T={T}, P={P} override)"), "desc": c["desc"], "T": T, "H": H, "k": K, "E": E, "P": P,
                    "zero_copy_const": [c["Z"], c["C"], c["Kc"]], "quant_mode": qm,
+                   "smooth": ("expert [E, H]" if sets[0]["smooth"] is not None and sets[0]["smooth"].ndim == 2
+                              else "channel [H]" if sets[0]["smooth"] is not None else "none"),
                    "num_max_dispatch_tokens_per_rank": c["num_max"], "seed": args.seed,
                    "rotating_input_sets": len(gsets), "rows_N": n_avg,
                    "launch": "hip_graph" if graphs is not None else "eager",

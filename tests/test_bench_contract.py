@@ -23,7 +23,7 @@ def test_dispatch_bytes_match_the_worked_example():
 def test_algorithmic_bytes_of_the_decode_workload():
     T, H, K = 4096, 7168, 8
     n = T * K
-    d = bench.dispatch_hbm_bytes(T, H, K, n, T, 2, True)
+    d = bench.dispatch_hbm_bytes(T, H, K, n, T, 2, 1)
     assert d == T * 2 * H + T * K * 4 + 4 * H + n * (H + 4)
     c = bench.combine_hbm_bytes(T, H, K, n, 0)
     assert c == n * 2 * H + T * K * 12 + T * 2 * H

@@ -357,3 +357,16 @@ def test_two_launch_layout_for_large_worlds(stride):
         rows = np.sort(lo["dst_row"][lo["dst_row"] >= 0])
         g["src_info"], lo["src_info"] = g["src_info"][rows], lo["src_info"][rows]
     G.assert_layout_equal(g, lo)
+
+
+@pytest.mark.parametrize("qm", [1, 2])
+def test_per_expert_smooth_scales_full_size(qm):
+    # the decode workload with [E, H] smooth scales (each copy quantized with its expert's row)
+    inp = workloads.make_inputs(2, seed=5)
+    c = inp["cfg"]
+    smooth = workloads.rng_for(5, 2, 4).uniform(0.5, 1.5, (c["E"], c["H"])).astype(np.float32)
+    y_fn = lambda lo, do: workloads.expert_out_normal(lo["num_rows"], c["H"], seed=5)
+    g, o = G.run_case(c["T"], c["H"], c["K"], c["E"], c["P"], 0, 0, 0, inp["topk_idx"], None, inp["x"],
+                      inp["topk_weights"], qm, smooth, y_fn, num_max=c["num_max"],
+                      label=f"per-expert smooth, quant {qm}")
+    G.assert_case(g, o, qm)
