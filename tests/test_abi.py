@@ -88,3 +88,24 @@ def test_rank_capacity_agrees_with_the_oracle(kw):
     args = (kw["T"], kw["H"], kw["K"], kw["E"], kw["P"], kw.get("Z", 0), kw.get("C", 0),
             kw.get("Kc", 0), kw.get("num_max", 0))
     assert mg.rank_capacity(mg.make_shape(*args)) == oracle.rank_capacity(oracle.make_shape(*args))
+
+
+def test_header_is_plain_c_and_a_c_client_links(tmp_path):
+    """moe_get.h compiles as C11 with gcc, and a C program calling layout,
+    dispatch and combine links against libmoe_get.so (no GPU work is run)."""
+    import importlib.util
+    import shutil
+    import subprocess
+
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_client", "build.py")
+    spec = importlib.util.spec_from_file_location("moe_c_client_build", path)
+    cb = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(cb)
+    cb.build()
+    assert os.access(cb.BIN, os.X_OK)
+    nm = subprocess.run(["nm", "-D", "--undefined-only", cb.BIN], capture_output=True, text=True)
+    if nm.returncode == 0:
+        for n in ("moe_get_layout", "moe_dispatch", "moe_combine"):
+            assert n in nm.stdout
