@@ -17,6 +17,8 @@
 //    bf16 in, 16 bytes of codes out, so every store instruction of a wave
 //    writes 1 KB contiguous); the dynamic scale needs the row's amax: a wave
 //    max, then a max over the <= 8 waves through LDS.
+//  - int8 with per-expert scales: one workgroup per (token, expert group), the
+//    copies quantized one at a time (see dispatch_quant_expert_kernel).
 // Loads are ordinary (the row is read once, K stores reuse it from VGPRs);
 // stores are non-temporal: receive rows are written once and read by a later
 // kernel.
@@ -72,127 +74,167 @@ __global__ void __launch_bounds__(256) dispatch_copy_kernel(DispatchArgs a, int 
 
 // ---- int8 (static or dynamic) -----------------------------------------------
 // one workgroup per token, blockDim = 64 * ceil(pairs / 64) <= 512; lane p of the
-// block owns channels [16p, 16p + 16) (chunks 2p and 2p + 1)
-template <int MODE, bool PER_EXPERT>
-__global__ void __launch_bounds__(512) dispatch_quant_kernel(DispatchArgs a) {
-  __shared__ float red[8][16];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
-  const int t = blockIdx.x;
-  const int K = a.K, H = a.H, nch = H >> 3;
-
-  int myrow = -1;
-  if (lane < K) myrow = a.dst_row[(size_t)t * K + lane];
-  uint64_t valid = ballot(myrow >= 0);
-  if (valid == 0ull) return;  // same for every wave of the block: no barrier is skipped
-  const bool write_w = wv == 0 && myrow >= 0 && a.expand_w;
-
-  const int p = threadIdx.x;
-  const int c0 = 2 * p, c1 = 2 * p + 1;
-  const bool has0 = c0 < nch, has1 = c1 < nch;
-  const int l0 = has0 ? c0 : 0, l1 = has1 ? c1 : 0;  // in-bounds chunks for lanes past the row end
-  const bool wide = (H & 15) == 0;                    // 16-byte code stores stay aligned
-  // every load of the lane is issued before the first use: row chunks, then scales
-  const u32x4 *xr = (const u32x4 *)(a.x + (size_t)t * H);
-  const u32x4 v0 = xr[l0], v1 = xr[l1];
-  f32x4 s4[4] = {f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f},
-                 f32x4{1.f, 1.f, 1.f, 1.f}};
-  auto load_scales = [&](const float *s) {
+// block owns channels [16p, 16p + 16) (chunks 2p and 2p + 1).  One code row per
+// token (no smoothing, or one smooth vector for all experts), stored to every
+// routed copy.
+struct QuantLane {
+  int p, l0, l1;
+  bool has0, has1, wide;
+  __device__ QuantLane(int H) {
+    const int nch = H >> 3;
+    p = threadIdx.x;
+    has0 = 2 * p < nch;
+    has1 = 2 * p + 1 < nch;
+    l0 = has0 ? 2 * p : 0;  // in-bounds chunks for lanes past the row end
+    l1 = has1 ? 2 * p + 1 : 0;
+    wide = (H & 15) == 0;  // 16-byte code stores stay aligned
+  }
+  __device__ void load_scales(const float *s, f32x4 *s4) const {
     const f32x4 *sp = (const f32x4 *)s;
     s4[0] = sp[2 * l0];
     s4[1] = sp[2 * l0 + 1];
     s4[2] = sp[2 * l1];
     s4[3] = sp[2 * l1 + 1];
-  };
-  if (!PER_EXPERT && a.smooth) load_scales(a.smooth);
-  float f[16];
-  unpack8(v0, f);
-  unpack8(v1, f + 8);
-
+  }
   // g = fp32(x) * scales, zero on channels past the row end
-  auto scale16 = [&](float *g) {
+  __device__ void scale16(const float *f, const f32x4 *s4, float *g) const {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const f32x4 &sv = s4[e >> 2];
       const float sc = (e & 3) == 0 ? sv.x : (e & 3) == 1 ? sv.y : (e & 3) == 2 ? sv.z : sv.w;
       g[e] = ((e < 8) ? has0 : has1) ? f[e] * sc : 0.0f;
     }
-  };
-  auto block_amax = [&](const float *g, int slot) {
-    float m = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(g[e]));
-    m = wave_max(m);
-    if (lane == 0) red[wv][slot] = m;
-  };
-  auto store_codes = [&](const float *g, float dyn, int row) {
+  }
+  template <int MODE>
+  __device__ void store_codes(const float *g, float dyn, int8_t *row_base) const {
     int cd[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) cd[e] = sat_code(MODE == 2 ? g[e] * dyn : g[e]);
     const u32x2 lo = u32x2{pack_i8x4(cd[0], cd[1], cd[2], cd[3]), pack_i8x4(cd[4], cd[5], cd[6], cd[7])};
     const u32x2 hi = u32x2{pack_i8x4(cd[8], cd[9], cd[10], cd[11]), pack_i8x4(cd[12], cd[13], cd[14], cd[15])};
-    int8_t *dst = (int8_t *)a.expand_x + (size_t)row * H + (size_t)p * 16;
+    int8_t *dst = row_base + (size_t)p * 16;
     if (wide && has1) {
       __builtin_nontemporal_store((u32x4{lo.x, lo.y, hi.x, hi.y}), (u32x4 *)dst);
     } else {
       if (has0) __builtin_nontemporal_store(lo, (u32x2 *)dst);
       if (has1) __builtin_nontemporal_store(hi, (u32x2 *)(dst + 8));
     }
-  };
+  }
+};
 
-  if constexpr (!PER_EXPERT) {
-    // one code row per token, written to every routed copy
-    float g[16];
-    scale16(g);
-    float dyn = 1.0f;
-    if constexpr (MODE == 2) {
-      block_amax(g, 0);
-      __syncthreads();
-      float amax = red[0][0];
-      for (int w2 = 1; w2 < nw; ++w2) amax = fmaxf(amax, red[w2][0]);
-      dyn = amax > 0.0f ? 127.0f / amax : 0.0f;
-      const float scale = amax > 0.0f ? 1.0f / dyn : 0.0f;
-      if (wv == 0 && myrow >= 0 && a.dyn_scales) a.dyn_scales[myrow] = scale;
-    }
-    while (valid) {
-      const int j = __builtin_ctzll(valid);
-      valid &= valid - 1;
-      store_codes(g, dyn, readlane(myrow, j));
-    }
-  } else {
-    // per-expert smooth scales: each copy is quantized with its expert's row
-    int myid = 0;
-    if (lane < K) myid = a.topk_idx[(size_t)t * K + lane];
-    if constexpr (MODE == 2) {
-      uint64_t m = valid;
-      while (m) {
-        const int j = __builtin_ctzll(m);
-        m &= m - 1;
-        float g[16];
-        load_scales(a.smooth + (size_t)readlane(myid, j) * H);
-        scale16(g);
-        block_amax(g, j);
-      }
-      __syncthreads();
-    }
-    while (valid) {
-      const int j = __builtin_ctzll(valid);
-      valid &= valid - 1;
-      const int row = readlane(myrow, j);
-      float g[16];
-      load_scales(a.smooth + (size_t)readlane(myid, j) * H);
-      scale16(g);
-      float dyn = 1.0f;
-      if constexpr (MODE == 2) {
-        float amax = red[0][j];
-        for (int w2 = 1; w2 < nw; ++w2) amax = fmaxf(amax, red[w2][j]);
-        dyn = amax > 0.0f ? 127.0f / amax : 0.0f;
-        if (threadIdx.x == j && a.dyn_scales) a.dyn_scales[row] = amax > 0.0f ? 1.0f / dyn : 0.0f;
-      }
-      store_codes(g, dyn, row);
-    }
+// max over the block of the per-wave maxima in red[0..nw)
+__device__ __forceinline__ float block_max_of(const float *red, int nw) {
+  float m = red[0];
+  for (int w = 1; w < nw; ++w) m = fmaxf(m, red[w]);
+  return m;
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(512) dispatch_quant_kernel(DispatchArgs a) {
+  __shared__ float red[8];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int t = blockIdx.x;
+  const int K = a.K, H = a.H;
+
+  int myrow = -1;
+  if (lane < K) myrow = a.dst_row[(size_t)t * K + lane];
+  uint64_t valid = ballot(myrow >= 0);
+  if (valid == 0ull) return;  // same for every wave of the block: no barrier is skipped
+
+  const QuantLane q(H);
+  // every load of the lane is issued before the first use: row chunks, then scales
+  const u32x4 *xr = (const u32x4 *)(a.x + (size_t)t * H);
+  const u32x4 v0 = xr[q.l0], v1 = xr[q.l1];
+  f32x4 s4[4] = {f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f},
+                 f32x4{1.f, 1.f, 1.f, 1.f}};
+  if (a.smooth) q.load_scales(a.smooth, s4);
+  float f[16], g[16];
+  unpack8(v0, f);
+  unpack8(v1, f + 8);
+  q.scale16(f, s4, g);
+  float dyn = 1.0f;
+  if constexpr (MODE == 2) {
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(g[e]));
+    m = wave_max(m);
+    if (lane == 0) red[wv] = m;
+    __syncthreads();
+    const float amax = block_max_of(red, nw);
+    dyn = amax > 0.0f ? 127.0f / amax : 0.0f;
+    if (wv == 0 && myrow >= 0 && a.dyn_scales) a.dyn_scales[myrow] = amax > 0.0f ? 1.0f / dyn : 0.0f;
+  }
+  const bool write_w = wv == 0 && myrow >= 0 && a.expand_w;
+  while (valid) {
+    const int j = __builtin_ctzll(valid);
+    valid &= valid - 1;
+    q.store_codes<MODE>(g, dyn, (int8_t *)a.expand_x + (size_t)readlane(myrow, j) * H);
   }
   if (write_w) a.expand_w[myrow] = a.w ? a.w[(size_t)t * K + lane] : 1.0f;
+}
+
+// ---- int8 with per-expert smooth scales [E, H] --------------------------------
+// Every copy is quantized with its own expert's scale row, so a token yields up to
+// K different code rows.  The scale matrix (E * H * 4 bytes, 7.3 MB at E = 256,
+// H = 7168) is larger than one XCD's L2; scale rows are re-read for every copy,
+// so where they are served from decides the speed.  Block b handles token b / G
+// and only the copies whose expert id e has e % G == b % G; workgroups are placed
+// on the 8 XCDs round-robin by block id, so with G = 2 each XCD's L2 sees half of
+// the scale rows.  (G = 8, one eighth per XCD, measured slower on gfx950: the
+// token row is then fetched by every XCD and many blocks have little work.)
+// Copies are quantized one at a time with the codes kept in registers across the
+// block-wide amax, so each scale row is read once per copy.
+constexpr int kExpertGroups = 2;
+
+template <int MODE>
+__global__ void __launch_bounds__(512) dispatch_quant_expert_kernel(DispatchArgs a) {
+  __shared__ float red[2][8];  // alternated per copy: one barrier per copy suffices
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int t = blockIdx.x / kExpertGroups, grp = blockIdx.x % kExpertGroups;
+  const int K = a.K, H = a.H;
+
+  int myrow = -1, myid = 0;
+  if (lane < K) {
+    myrow = a.dst_row[(size_t)t * K + lane];
+    myid = a.topk_idx[(size_t)t * K + lane];
+  }
+  const bool mine = myrow >= 0 && myid % kExpertGroups == grp;  // routed rows have 0 <= id < E
+  uint64_t sel = ballot(mine);
+  if (sel == 0ull) return;  // same for every wave of the block
+
+  const QuantLane q(H);
+  const u32x4 *xr = (const u32x4 *)(a.x + (size_t)t * H);
+  const u32x4 v0 = xr[q.l0], v1 = xr[q.l1];
+  if (wv == 0 && mine && a.expand_w) a.expand_w[myrow] = a.w ? a.w[(size_t)t * K + lane] : 1.0f;
+  float f[16];
+  unpack8(v0, f);
+  unpack8(v1, f + 8);
+  int par = 0;
+  while (sel) {
+    const int j = __builtin_ctzll(sel);
+    sel &= sel - 1;
+    const int row = readlane(myrow, j);
+    f32x4 s4[4];
+    q.load_scales(a.smooth + (size_t)readlane(myid, j) * H, s4);
+    float g[16];
+    q.scale16(f, s4, g);
+    float dyn = 1.0f;
+    if constexpr (MODE == 2) {
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(g[e]));
+      m = wave_max(m);
+      if (lane == 0) red[par][wv] = m;
+      __syncthreads();
+      const float amax = block_max_of(red[par], nw);
+      par ^= 1;
+      dyn = amax > 0.0f ? 127.0f / amax : 0.0f;
+      if (threadIdx.x == 0 && a.dyn_scales) a.dyn_scales[row] = amax > 0.0f ? 1.0f / dyn : 0.0f;
+    }
+    q.store_codes<MODE>(g, dyn, (int8_t *)a.expand_x + (size_t)row * H);
+  }
 }
 
 hipError_t launch_dispatch(const DispatchArgs &a, int quant_mode, bool per_expert, hipStream_t stream) {
@@ -207,15 +249,15 @@ hipError_t launch_dispatch(const DispatchArgs &a, int quant_mode, bool per_exper
   }
   const int pairs = (nch + 1) / 2;  // <= 512 for H <= 8192
   const dim3 blk(64 * ((pairs + 63) / 64));
-  const dim3 g((unsigned)a.T);
+  const dim3 g((unsigned)a.T), ge((unsigned)((int64_t)a.T * kExpertGroups));
   if (quant_mode == 1 && !per_expert)
-    hipLaunchKernelGGL((dispatch_quant_kernel<1, false>), g, blk, 0, stream, a);
+    hipLaunchKernelGGL((dispatch_quant_kernel<1>), g, blk, 0, stream, a);
   else if (quant_mode == 1)
-    hipLaunchKernelGGL((dispatch_quant_kernel<1, true>), g, blk, 0, stream, a);
+    hipLaunchKernelGGL((dispatch_quant_expert_kernel<1>), ge, blk, 0, stream, a);
   else if (!per_expert)
-    hipLaunchKernelGGL((dispatch_quant_kernel<2, false>), g, blk, 0, stream, a);
+    hipLaunchKernelGGL((dispatch_quant_kernel<2>), g, blk, 0, stream, a);
   else
-    hipLaunchKernelGGL((dispatch_quant_kernel<2, true>), g, blk, 0, stream, a);
+    hipLaunchKernelGGL((dispatch_quant_expert_kernel<2>), ge, blk, 0, stream, a);
   return hipGetLastError();
 }
 
