@@ -113,7 +113,13 @@ def cpu_baseline(inp, target_seconds):
         n = lo["num_rows"]
         total_comm += dispatch_comm_bytes(n, c["H"], c["quant_mode"]) + combine_comm_bytes(n, c["H"])
         reps += 1
-    return dict(value=round(total_comm / 1e9 / dt, 3), unit="GB/s", cores=1, kind="oracle",
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return dict(value=round(total_comm / 1e9 / dt, 3), unit="GB/s", cores=1, kind="oracle", cpu_model=model,
                 sample=f"{reps} whole passes (layout + dispatch + combine) of the timed workload, "
                        f"{dt:.1f} s single-threaded; oracle combine in float64",
                 seconds_per_pass=round(dt / reps, 4))
@@ -292,63 +298,15 @@ def run_dbo(args):
                       "results": results}), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--tokens", type=int, default=None, help="override T (a multiple of the rank count)")
-    ap.add_argument("--quant", type=int, default=None, choices=[0, 1, 2], help="override the quant mode")
-    ap.add_argument("--smooth", default=None, choices=["none", "channel", "expert"],
-                    help="override the smooth scales: none, one [H] vector, or [E, H] per expert")
-    ap.add_argument("--ranks", type=int, default=None,
-                    help="override P; with --tokens equal to one rank's batch this times one rank's share")
-    ap.add_argument("--rotate", type=int, default=2, help="input sets cycled through (defeats cache reuse)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--rank-stride", default="0",
-                    help="receive layout: 0 compact rows; 'min' or an integer A >= the rank capacity "
-                         "puts rank r's rows in the fixed window [r A, r A + A)")
-    ap.add_argument("--graph", action="store_true",
-                    help="capture one step per input set in a HIP graph and time graph replays "
-                         "(every replay is checked bit for bit against the eager step)")
-    ap.add_argument("--dbo", action="store_true",
-                    help="dual-batch overlap measurement instead of the step benchmark (prints its own JSON line)")
-    ap.add_argument("--dbo-f", default="256,512,2048", help="expert intermediate sizes F for --dbo")
-    ap.add_argument("--dbo-comm-cus", default="0",
-                    help="CUs given to the data-movement stream in --dbo (0: no split; a split needs CU-masked streams)")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="after timing, run a plain 512 MiB device copy 3x (counter calibration)")
-    args = ap.parse_args()
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py: this MoE dispatch/combine path runs on one GPU only; --gpus above 1 is not "
-              "supported (the simulated expert-parallel world of P ranks lives on the one GPU).",
-              file=sys.stderr, flush=True)
-        sys.exit(2)
-
-    if args.dbo:
-        run_dbo(args)
-        return
-
+def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False):
+    """One step benchmark of a workload (tokens / ranks override T and P); returns the JSON
+    line without cpu_baseline, and the first input set."""
     import torch
-
-    import combine_moe_get_amd as mg
-    from combine_moe_get_amd import workloads
-
-    if not os.path.exists(mg.LIB_PATH):
-        import __graft_entry__
-        __graft_entry__.build()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
 
     cid = args.workload
     sets = []
     for r in range(args.rotate):
-        inp = workloads.make_inputs(cid, seed=args.seed + r, T=args.tokens, P=args.ranks)
+        inp = workloads.make_inputs(cid, seed=args.seed + r, T=tokens, P=ranks)
         sets.append(inp)
     c = sets[0]["cfg"]
     T, H, K, E, P, qm = c["T"], c["H"], c["K"], c["E"], c["P"], c["quant_mode"]
@@ -513,7 +471,9 @@ def main():
 
     def kstats(k_ms, call_ms, comm, hbm):
         d = dict(kernel_us=round(k_ms * 1e3, 2), in_step_us=round(float(call_ms.mean()) * 1e3, 2),
-                 in_step_us_median=round(float(np.median(call_ms)) * 1e3, 2))
+                 in_step_us_median=round(float(np.median(call_ms)) * 1e3, 2),
+                 in_step_us_min=round(float(call_ms.min()) * 1e3, 2),
+                 in_step_us_p90=round(float(np.percentile(call_ms, 90)) * 1e3, 2))
         if comm is not None:
             d.update(comm_bytes=int(comm), hbm_bytes=int(hbm),
                      comm_GBps=round(comm / 1e9 / (k_ms * 1e-3), 1), hbm_GBps=round(hbm / 1e9 / (k_ms * 1e-3), 1))
@@ -523,7 +483,7 @@ def main():
 
     kern = {"dispatch": kstats(k_dis, dis_ms, cb_d, hb_d), "combine": kstats(k_com, com_ms, cb_c, hb_c),
             "layout": kstats(k_lay, lay_ms, None, None)}
-    kern["layout"]["launches"] = 2
+    kern["layout"]["launches"] = mg.layout_launches(shape)
     dom = "combine" if k_com >= k_dis else "dispatch"
     ach = kern[dom]["hbm_GBps"]
     traffic = counter_traffic(dom, c["name"])
@@ -533,7 +493,7 @@ def main():
                     algorithmic_bytes_per_launch=kern[dom]["hbm_bytes"],
                     kernel_us=kern[dom]["kernel_us"])
 
-    if args.copy_probe:
+    if copy_probe:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
@@ -553,7 +513,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded generators; no dataset or weights)",
-        "config": {"workload": c["name"] + ("" if args.tokens is None and args.ranks is None else
+        "config": {"workload": c["name"] + ("" if tokens is None and ranks is None else
                                             f" (T={T}, P={P} override)"), "desc": c["desc"], "T": T, "H": H, "k": K, "E": E, "P": P,
                    "zero_copy_const": [c["Z"], c["C"], c["Kc"]], "quant_mode": qm,
                    "smooth": ("expert [E, H]" if sets[0]["smooth"] is not None and sets[0]["smooth"].ndim == 2
@@ -569,8 +529,76 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    return line, sets[0]
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--tokens", type=int, default=None, help="override T (a multiple of the rank count)")
+    ap.add_argument("--quant", type=int, default=None, choices=[0, 1, 2], help="override the quant mode")
+    ap.add_argument("--smooth", default=None, choices=["none", "channel", "expert"],
+                    help="override the smooth scales: none, one [H] vector, or [E, H] per expert")
+    ap.add_argument("--ranks", type=int, default=None,
+                    help="override P; with --tokens equal to one rank's batch this times one rank's share")
+    ap.add_argument("--rotate", type=int, default=2, help="input sets cycled through (defeats cache reuse)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rank-stride", default="0",
+                    help="receive layout: 0 compact rows; 'min' or an integer A >= the rank capacity "
+                         "puts rank r's rows in the fixed window [r A, r A + A)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step per input set in a HIP graph and time graph replays "
+                         "(every replay is checked bit for bit against the eager step)")
+    ap.add_argument("--dbo", action="store_true",
+                    help="dual-batch overlap measurement instead of the step benchmark (prints its own JSON line)")
+    ap.add_argument("--dbo-f", default="256,512,2048", help="expert intermediate sizes F for --dbo")
+    ap.add_argument("--dbo-comm-cus", default="0",
+                    help="CUs given to the data-movement stream in --dbo (0: no split; a split needs CU-masked streams)")
+    ap.add_argument("--no-share", action="store_true",
+                    help="skip the extra measurement of one rank's share (T = BS, P = 1)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, run a plain 512 MiB device copy 3x (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this MoE dispatch/combine path runs on one GPU only; --gpus above 1 is not "
+              "supported (the simulated expert-parallel world of P ranks lives on the one GPU).",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    if args.dbo:
+        run_dbo(args)
+        return
+
+    import torch
+
+    import combine_moe_get_amd as mg
+    from combine_moe_get_amd import workloads
+
+    if not os.path.exists(mg.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    line, inp0 = measure(args, mg, workloads, dev, args.tokens, args.ranks, copy_probe=args.copy_probe)
+    if args.tokens is None and args.ranks is None and not args.no_share and not args.graph:
+        # one simulated rank's share at its real shape: its BS tokens, all E experts local
+        bs = line["config"]["T"] // line["config"]["P"]
+        sh, _ = measure(args, mg, workloads, dev, bs, 1)
+        line["one_rank_share"] = dict(
+            T=bs, P=1, us_per_layer=sh["us_per_layer"],
+            kernel_us={k: v["kernel_us"] for k, v in sh["kernels"].items()},
+            in_step_us_median={k: v["in_step_us_median"] for k, v in sh["kernels"].items()},
+            layout_launches=sh["kernels"]["layout"]["launches"])
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(sets[0], args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(inp0, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

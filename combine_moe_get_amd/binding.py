@@ -102,6 +102,8 @@ def lib():
         L.moe_get_layout_ex.restype = ctypes.c_int
         L.moe_get_rank_capacity.argtypes = [SP]
         L.moe_get_rank_capacity.restype = I64
+        L.moe_get_layout_launches.argtypes = [SP]
+        L.moe_get_layout_launches.restype = ctypes.c_int
         L.moe_dispatch.argtypes = [SP, I32, V, V, I32, V, V, V, V, V, V, V]
         L.moe_dispatch.restype = ctypes.c_int
         L.moe_combine.argtypes = [SP] + [V] * 11
@@ -133,6 +135,14 @@ def workspace_size(shape):
 def rank_capacity(shape):
     """Smallest per-rank receive window of the fixed-capacity layout (moe_get_rank_capacity)."""
     return lib().moe_get_rank_capacity(ctypes.byref(shape))
+
+
+def layout_launches(shape):
+    """Kernel launches moe_get_layout makes for this shape (moe_get_layout_launches)."""
+    n = lib().moe_get_layout_launches(ctypes.byref(shape))
+    if n < 0:
+        raise MoeGetError("moe_get_layout_launches", n)
+    return n
 
 
 def _stream(stream):

@@ -96,6 +96,33 @@ int64_t moe_get_rank_capacity(const moe_get_shape_t *shape) {
   return nm * P * (L < shape->topk ? L : shape->topk);
 }
 
+// the size fields of the layout kernels' arguments (pointers null)
+static LayoutArgs layout_sizes(const moe_get_shape_t *shape) {
+  LayoutArgs a;
+  memset(&a, 0, sizeof a);
+  const int T = shape->num_tokens, K = shape->topk, E = shape->num_experts, P = shape->num_ranks;
+  const int NS = n_special(shape);
+  a.T = T;
+  a.K = K;
+  a.E = E;
+  a.P = P;
+  a.BS = T / P;
+  a.L = E / P;
+  a.NS = NS;
+  a.nbits = 32 - __builtin_clz((unsigned)E);  // bits of the sentinel key E
+  a.Epad = E + (E & 1);
+  const int S = a.BS * K;
+  a.Spad = S + (S & 1);
+  a.Etot = (int64_t)E + NS;
+  return a;
+}
+
+int moe_get_layout_launches(const moe_get_shape_t *shape) {
+  const int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  return layout_launch_count(layout_sizes(shape));
+}
+
 size_t moe_get_workspace_size(const moe_get_shape_t *shape) {
   if (check_shape(shape) != MOE_OK) return 0;
   return ws_layout(shape).total;
@@ -136,22 +163,9 @@ int moe_get_layout_ex(const moe_get_shape_t *shape, int64_t rank_stride, const i
   if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & (kAlign - 1)) != 0)
     return MOE_ERR_ARG;
 
-  LayoutArgs a;
-  memset(&a, 0, sizeof a);
+  LayoutArgs a = layout_sizes(shape);
   a.topk_idx = topk_idx;
   a.mask = x_active_mask;
-  a.T = T;
-  a.K = K;
-  a.E = E;
-  a.P = P;
-  a.BS = T / P;
-  a.L = E / P;
-  a.NS = NS;
-  a.nbits = 32 - __builtin_clz((unsigned)E);  // bits of the sentinel key E
-  a.Epad = E + (E & 1);
-  const int S = a.BS * K;
-  a.Spad = S + (S & 1);
-  a.Etot = (int64_t)E + NS;
   a.rank_stride = rank_stride;
   a.cnt = num_tokens_per_expert;
   a.expert_offsets = expert_offsets;

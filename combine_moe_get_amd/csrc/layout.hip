@@ -537,11 +537,18 @@ size_t layout_fused_lds_bytes(int waves, int E, int NS, int Epad, int Spad, int 
          (size_t)waves * Epad * 2 + (size_t)Spad * 2 + (size_t)BS;
 }
 
+// single launch while each workgroup's pass over every token stays small
+static bool use_fused(const LayoutArgs &a) {
+  const size_t flds = layout_fused_lds_bytes(layout_waves(a.E), a.E, a.NS, a.Epad, a.Spad, a.P, a.BS);
+  return (int64_t)a.T * a.K <= kFusedMaxSlots && flds <= kMaxLds;
+}
+
+int layout_launch_count(const LayoutArgs &a) { return use_fused(a) ? 1 : 2; }
+
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {
   const int W = layout_waves(a.E);
-  // single launch while each workgroup's pass over every token stays small
   const size_t flds = layout_fused_lds_bytes(W, a.E, a.NS, a.Epad, a.Spad, a.P, a.BS);
-  if ((int64_t)a.T * a.K <= kFusedMaxSlots && flds <= kMaxLds) {
+  if (use_fused(a)) {
     const void *fn = W == 16 ? (const void *)&layout_fused_kernel<16> : (const void *)&layout_fused_kernel<8>;
     if (flds > 65536) {
       const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)flds);

@@ -94,6 +94,7 @@ struct CombineArgs {
 // ---- launchers (return hipSuccess or the launch error) ---------------------
 
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream);
+int layout_launch_count(const LayoutArgs &a);  // kernels launch_layout runs for these sizes
 hipError_t launch_dispatch(const DispatchArgs &a, int quant_mode, bool per_expert, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
 

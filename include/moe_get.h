@@ -100,6 +100,12 @@ int64_t moe_get_recv_capacity(const moe_get_shape_t *shape);
  * num_max_dispatch_tokens_per_rank is 0.  Returns -1 for an invalid shape. */
 int64_t moe_get_rank_capacity(const moe_get_shape_t *shape);
 
+/* Kernel launches one moe_get_layout / moe_get_layout_ex call makes for this
+ * shape: 1 (T * K <= 8192 slots: every workgroup histograms all ids itself)
+ * or 2 (a count kernel, then a scan-and-finalize kernel).  For profiling and
+ * launch accounting only; a negative MOE_ERR_* for an invalid shape. */
+int moe_get_layout_launches(const moe_get_shape_t *shape);
+
 /* Bytes of device workspace moe_get_layout needs (0 for an invalid shape). */
 size_t moe_get_workspace_size(const moe_get_shape_t *shape);
 

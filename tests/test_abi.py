@@ -109,3 +109,13 @@ def test_header_is_plain_c_and_a_c_client_links(tmp_path):
     if nm.returncode == 0:
         for n in ("moe_get_layout", "moe_dispatch", "moe_combine"):
             assert n in nm.stdout
+
+
+def test_layout_launches():
+    # one launch while T * K <= 8192 slots, two above; errors for shapes outside the constraints
+    assert mg.layout_launches(mg.make_shape(128, 7168, 8, 256, 1)) == 1
+    assert mg.layout_launches(mg.make_shape(1024, 7168, 8, 256, 32)) == 1
+    assert mg.layout_launches(mg.make_shape(1056, 7168, 8, 256, 32)) == 2
+    assert mg.layout_launches(mg.make_shape(4096, 7168, 8, 256, 32)) == 2
+    with pytest.raises(mg.MoeGetError):
+        mg.layout_launches(mg.make_shape(100, 7168, 8, 256, 32))  # T not a multiple of P
