@@ -375,6 +375,10 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False)
                                          g["ex"], g["ds"], rows=cap)
         g["c_com"] = mg.prepare_combine(shape, g["y"], g["topk"], g["w"], g["lay"].dst_row, g["mask"], g["ori"],
                                         g["a1"], g["a2"], g["v"], out=g["out"])
+        # the same layout + dispatch through the one-call entry point (same output buffers)
+        g["c_ld"] = mg.prepare_layout_dispatch(shape, qm, g["x"], g["topk"], g["mask"], g["smooth"], None,
+                                               out=g["lay"], expand_x=g["ex"], dynamic_scales=g["ds"],
+                                               workspace=g["ws"], rank_stride=A)
 
     def step(g, ev=None, st=None):
         st = stream if st is None else st
@@ -459,6 +463,26 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False)
     k_lay = kernel_avg_ms(lambda g: g["c_lay"](stream))
     status = max(int(g["lay"].status[0]) for g in gsets)
 
+    # the step with layout + dispatch through moe_layout_dispatch (one kernel for T * K <= 8192)
+    fused = None
+    if graphs is None:
+        def step_fused(g):
+            g["c_ld"](stream)
+            g["c_com"](stream)
+        for i in range(args.warmup):
+            step_fused(gsets[i % len(gsets)])
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        f0.record(stream)
+        for i in range(args.steps):
+            step_fused(gsets[i % len(gsets)])
+        f1.record(stream)
+        torch.cuda.synchronize()
+        k_ld = kernel_avg_ms(lambda g: g["c_ld"](stream))
+        fused = dict(us_per_layer=round(f0.elapsed_time(f1) / args.steps * 1e3, 2),
+                     layout_dispatch_kernel_us=round(k_ld * 1e3, 2),
+                     layout_dispatch_launches=mg.layout_dispatch_launches(shape))
+
     n_avg = float(np.mean([g["n"] for g in gsets]))
     cb_d = dispatch_comm_bytes(n_avg, H, qm)
     cb_c = combine_comm_bytes(n_avg, H)
@@ -529,6 +553,8 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False)
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if fused is not None:
+        line["fused_layout_dispatch"] = fused
     return line, sets[0]
 
 
@@ -596,7 +622,8 @@ def main():
             T=bs, P=1, us_per_layer=sh["us_per_layer"],
             kernel_us={k: v["kernel_us"] for k, v in sh["kernels"].items()},
             in_step_us_median={k: v["in_step_us_median"] for k, v in sh["kernels"].items()},
-            layout_launches=sh["kernels"]["layout"]["launches"])
+            layout_launches=sh["kernels"]["layout"]["launches"],
+            fused_layout_dispatch=sh.get("fused_layout_dispatch"))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp0, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -104,6 +104,10 @@ def lib():
         L.moe_get_rank_capacity.restype = I64
         L.moe_get_layout_launches.argtypes = [SP]
         L.moe_get_layout_launches.restype = ctypes.c_int
+        L.moe_layout_dispatch.argtypes = [SP, I64, I32, V, V, V, V, I32, V] + [V] * 12 + [V, V, SZ, V]
+        L.moe_layout_dispatch.restype = ctypes.c_int
+        L.moe_layout_dispatch_launches.argtypes = [SP]
+        L.moe_layout_dispatch_launches.restype = ctypes.c_int
         L.moe_dispatch.argtypes = [SP, I32, V, V, I32, V, V, V, V, V, V, V]
         L.moe_dispatch.restype = ctypes.c_int
         L.moe_combine.argtypes = [SP] + [V] * 11
@@ -142,6 +146,14 @@ def layout_launches(shape):
     n = lib().moe_get_layout_launches(ctypes.byref(shape))
     if n < 0:
         raise MoeGetError("moe_get_layout_launches", n)
+    return n
+
+
+def layout_dispatch_launches(shape):
+    """Kernel launches moe_layout_dispatch makes for this shape (moe_layout_dispatch_launches)."""
+    n = lib().moe_layout_dispatch_launches(ctypes.byref(shape))
+    if n < 0:
+        raise MoeGetError("moe_layout_dispatch_launches", n)
     return n
 
 
@@ -316,3 +328,70 @@ def combine(shape, expert_out, topk_idx, topk_weights, dst_row, x_active_mask=No
     """moe_combine.  Returns out [T, H] bf16."""
     return prepare_combine(shape, expert_out, topk_idx, topk_weights, dst_row, x_active_mask, ori_x,
                            const_alpha1, const_alpha2, const_v, out)(stream)
+
+
+def _smooth_rows(shape, x_smooth_scale):
+    H, E = shape.hidden, shape.num_experts
+    if x_smooth_scale is None:
+        return 0
+    n = 1 if x_smooth_scale.numel() == H else x_smooth_scale.numel() // H
+    if n * H != x_smooth_scale.numel() or n not in (1, E):
+        raise ValueError("x_smooth_scale must hold [H] or [num_experts, H] floats")
+    return n
+
+
+def prepare_layout_dispatch(shape, quant_mode, x, topk_idx, x_active_mask=None, x_smooth_scale=None,
+                            topk_weights=None, out=None, expand_x=None, dynamic_scales=None, expand_weights=None,
+                            workspace=None, rank_stride=0):
+    """Checked, marshalled moe_layout_dispatch call; see layout_dispatch()."""
+    st = check_shape(shape)
+    if st != MOE_OK:
+        raise MoeGetError("layout_dispatch", st)
+    T, H, K, E, P = shape.num_tokens, shape.hidden, shape.topk, shape.num_experts, shape.num_ranks
+    dev = topk_idx.device
+    rows = P * rank_stride if rank_stride > 0 else T * K
+    cap = max(rows, 1)
+    out = out if out is not None else alloc_layout(shape, dev, rank_stride)
+    workspace = workspace if workspace is not None else alloc_workspace(shape, dev)
+    if expand_x is None:
+        expand_x = torch.empty((cap, H), dtype=torch.bfloat16 if quant_mode == 0 else torch.int8, device=dev)
+    if quant_mode == QUANT_DYNAMIC_INT8 and dynamic_scales is None:
+        dynamic_scales = torch.empty(cap, dtype=torch.float32, device=dev)
+    args = [
+        ctypes.byref(shape), ctypes.c_int64(int(rank_stride)), int(quant_mode),
+        _ptr(topk_idx, "topk_idx", I32, T * K),
+        _ptr(x_active_mask, "x_active_mask", U8, T, required=False),
+        _ptr(x, "x", BF16, T * H),
+        _ptr(x_smooth_scale, "x_smooth_scale", F32, required=False),
+        _smooth_rows(shape, x_smooth_scale),
+        _ptr(topk_weights, "topk_weights", F32, T * K, required=False),
+        _ptr(out.num_tokens_per_expert, "num_tokens_per_expert", I32, E),
+        _ptr(out.expert_offsets, "expert_offsets", I32, E + 1),
+        _ptr(out.recv_counts, "recv_counts", I32, E * P),
+        _ptr(out.special_counts, "special_counts", I32, shape.n_special, required=shape.n_special > 0),
+        _ptr(out.num_tokens_per_rank, "num_tokens_per_rank", I32, P),
+        _ptr(out.rank_offsets, "rank_offsets", I32, P + 1),
+        _ptr(out.is_token_in_rank, "is_token_in_rank", U8, T * P),
+        _ptr(out.dst_row, "dst_row", I32, T * K),
+        _ptr(out.src_info, "src_info", I32, rows),
+        _ptr(expand_x, "expand_x", BF16 if quant_mode == 0 else (torch.int8,), rows * H),
+        _ptr(dynamic_scales, "dynamic_scales", F32, rows, required=False),
+        _ptr(expand_weights, "expand_weights", F32, rows, required=False),
+        _ptr(out.status, "status", I32, 1),
+        _ptr(workspace, "workspace", (torch.uint8,)),
+        ctypes.c_size_t(workspace.numel()),
+        None,
+    ]
+    keep = (shape, x, topk_idx, x_active_mask, x_smooth_scale, topk_weights, workspace)
+    return PreparedCall(lib().moe_layout_dispatch, args, "moe_layout_dispatch", keep,
+                        (out, expand_x, dynamic_scales, expand_weights))
+
+
+def layout_dispatch(shape, quant_mode, x, topk_idx, x_active_mask=None, x_smooth_scale=None, topk_weights=None,
+                    out=None, expand_x=None, dynamic_scales=None, expand_weights=None, workspace=None,
+                    stream=None, rank_stride=0):
+    """moe_layout_dispatch: layout and dispatch in one call (one kernel for T * K <= 8192
+    slots).  Returns (Layout, expand_x, dynamic_scales or None, expand_weights or None),
+    identical to layout() followed by dispatch()."""
+    return prepare_layout_dispatch(shape, quant_mode, x, topk_idx, x_active_mask, x_smooth_scale, topk_weights,
+                                   out, expand_x, dynamic_scales, expand_weights, workspace, rank_stride)(stream)

@@ -140,19 +140,23 @@ int moe_get_layout(const moe_get_shape_t *shape, const int32_t *topk_idx,
                            stream);
 }
 
-int moe_get_layout_ex(const moe_get_shape_t *shape, int64_t rank_stride, const int32_t *topk_idx,
-                      const uint8_t *x_active_mask, int32_t *num_tokens_per_expert,
-                      int32_t *expert_offsets, int32_t *recv_counts, int32_t *special_counts,
-                      int32_t *num_tokens_per_rank, int32_t *rank_offsets,
-                      uint8_t *is_token_in_rank, int32_t *dst_row, int32_t *src_info,
-                      uint32_t *status_dev, void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// checks of moe_get_layout_ex's arguments; fills the kernel argument block
+int layout_args(const moe_get_shape_t *shape, int64_t rank_stride, const int32_t *topk_idx,
+                const uint8_t *x_active_mask, int32_t *num_tokens_per_expert, int32_t *expert_offsets,
+                int32_t *recv_counts, int32_t *special_counts, int32_t *num_tokens_per_rank,
+                int32_t *rank_offsets, uint8_t *is_token_in_rank, int32_t *dst_row, int32_t *src_info,
+                uint32_t *status_dev, void *workspace, size_t workspace_bytes, LayoutArgs &a) {
   const int st = check_shape(shape);
   if (st != MOE_OK) return st;
   if (rank_stride < 0) return MOE_ERR_ARG;
   if (rank_stride > 0 && (rank_stride < moe_get_rank_capacity(shape) ||
                           rank_stride * shape->num_ranks >= (int64_t)INT32_MAX))
     return MOE_ERR_CAPACITY;
-  const int T = shape->num_tokens, K = shape->topk, E = shape->num_experts, P = shape->num_ranks;
+  const int T = shape->num_tokens;
   const int NS = n_special(shape);
   if (!num_tokens_per_expert || !expert_offsets || !recv_counts || !num_tokens_per_rank ||
       !rank_offsets)
@@ -163,7 +167,7 @@ int moe_get_layout_ex(const moe_get_shape_t *shape, int64_t rank_stride, const i
   if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & (kAlign - 1)) != 0)
     return MOE_ERR_ARG;
 
-  LayoutArgs a = layout_sizes(shape);
+  a = layout_sizes(shape);
   a.topk_idx = topk_idx;
   a.mask = x_active_mask;
   a.rank_stride = rank_stride;
@@ -181,18 +185,20 @@ int moe_get_layout_ex(const moe_get_shape_t *shape, int64_t rank_stride, const i
   a.ws_rank_tok = (int32_t *)(ws + w.rank_tok);
   a.ws_special = (int32_t *)(ws + w.special);
   a.status = status_dev ? status_dev : (uint32_t *)(ws + w.status);
-  return launch_layout(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  return MOE_OK;
 }
 
-int moe_dispatch(const moe_get_shape_t *shape, int32_t quant_mode, const uint16_t *x,
-                 const float *x_smooth_scale, int32_t smooth_rows, const float *topk_weights,
-                 const int32_t *topk_idx, const int32_t *dst_row, void *expand_x,
-                 float *dynamic_scales, float *expand_weights, void *stream) {
+// checks of moe_dispatch's arguments; fills the kernel argument block and says whether the
+// scales are per expert
+int dispatch_args(const moe_get_shape_t *shape, int32_t quant_mode, const uint16_t *x,
+                  const float *x_smooth_scale, int32_t smooth_rows, const float *topk_weights,
+                  const int32_t *topk_idx, const int32_t *dst_row, void *expand_x, float *dynamic_scales,
+                  float *expand_weights, DispatchArgs &a, bool &per_expert) {
   const int st = check_shape(shape);
   if (st != MOE_OK) return st;
   if (quant_mode < 0 || quant_mode > 2) return MOE_ERR_ARG;
   const int T = shape->num_tokens, E = shape->num_experts;
-  bool per_expert = false;
+  per_expert = false;
   const float *smooth = nullptr;
   if (quant_mode != 0) {
     if (smooth_rows != 0 && smooth_rows != 1 && smooth_rows != E) return MOE_ERR_ARG;
@@ -203,11 +209,11 @@ int moe_dispatch(const moe_get_shape_t *shape, int32_t quant_mode, const uint16_
       if (per_expert && !topk_idx) return MOE_ERR_ARG;
     }
   }
-  if (T == 0) return MOE_OK;
-  if (!x || !dst_row || !expand_x) return MOE_ERR_ARG;
-  if (!aligned16(x) || !aligned16(expand_x)) return MOE_ERR_ARG;
-
-  DispatchArgs a;
+  memset(&a, 0, sizeof a);
+  if (T > 0) {
+    if (!x || !dst_row || !expand_x) return MOE_ERR_ARG;
+    if (!aligned16(x) || !aligned16(expand_x)) return MOE_ERR_ARG;
+  }
   a.x = x;
   a.smooth = smooth;
   a.w = topk_weights;
@@ -219,8 +225,67 @@ int moe_dispatch(const moe_get_shape_t *shape, int32_t quant_mode, const uint16_
   a.T = T;
   a.H = shape->hidden;
   a.K = shape->topk;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_get_layout_ex(const moe_get_shape_t *shape, int64_t rank_stride, const int32_t *topk_idx,
+                      const uint8_t *x_active_mask, int32_t *num_tokens_per_expert,
+                      int32_t *expert_offsets, int32_t *recv_counts, int32_t *special_counts,
+                      int32_t *num_tokens_per_rank, int32_t *rank_offsets,
+                      uint8_t *is_token_in_rank, int32_t *dst_row, int32_t *src_info,
+                      uint32_t *status_dev, void *workspace, size_t workspace_bytes, void *stream) {
+  LayoutArgs a;
+  const int st = layout_args(shape, rank_stride, topk_idx, x_active_mask, num_tokens_per_expert, expert_offsets,
+                             recv_counts, special_counts, num_tokens_per_rank, rank_offsets, is_token_in_rank,
+                             dst_row, src_info, status_dev, workspace, workspace_bytes, a);
+  if (st != MOE_OK) return st;
+  return launch_layout(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_dispatch(const moe_get_shape_t *shape, int32_t quant_mode, const uint16_t *x,
+                 const float *x_smooth_scale, int32_t smooth_rows, const float *topk_weights,
+                 const int32_t *topk_idx, const int32_t *dst_row, void *expand_x,
+                 float *dynamic_scales, float *expand_weights, void *stream) {
+  DispatchArgs a;
+  bool per_expert = false;
+  const int st = dispatch_args(shape, quant_mode, x, x_smooth_scale, smooth_rows, topk_weights, topk_idx, dst_row,
+                               expand_x, dynamic_scales, expand_weights, a, per_expert);
+  if (st != MOE_OK) return st;
+  if (a.T == 0) return MOE_OK;
   return launch_dispatch(a, quant_mode, per_expert, (hipStream_t)stream) == hipSuccess ? MOE_OK
                                                                                       : MOE_ERR_HIP;
+}
+
+int moe_layout_dispatch(const moe_get_shape_t *shape, int64_t rank_stride, int32_t quant_mode,
+                        const int32_t *topk_idx, const uint8_t *x_active_mask, const uint16_t *x,
+                        const float *x_smooth_scale, int32_t smooth_rows, const float *topk_weights,
+                        int32_t *num_tokens_per_expert, int32_t *expert_offsets, int32_t *recv_counts,
+                        int32_t *special_counts, int32_t *num_tokens_per_rank, int32_t *rank_offsets,
+                        uint8_t *is_token_in_rank, int32_t *dst_row, int32_t *src_info, void *expand_x,
+                        float *dynamic_scales, float *expand_weights, uint32_t *status_dev, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+  LayoutArgs la;
+  int st = layout_args(shape, rank_stride, topk_idx, x_active_mask, num_tokens_per_expert, expert_offsets,
+                       recv_counts, special_counts, num_tokens_per_rank, rank_offsets, is_token_in_rank, dst_row,
+                       src_info, status_dev, workspace, workspace_bytes, la);
+  if (st != MOE_OK) return st;
+  DispatchArgs da;
+  bool per_expert = false;
+  st = dispatch_args(shape, quant_mode, x, x_smooth_scale, smooth_rows, topk_weights, topk_idx, dst_row, expand_x,
+                     dynamic_scales, expand_weights, da, per_expert);
+  if (st != MOE_OK) return st;
+  return launch_layout_dispatch(la, da, quant_mode, per_expert, (hipStream_t)stream) == hipSuccess ? MOE_OK
+                                                                                                  : MOE_ERR_HIP;
+}
+
+int moe_layout_dispatch_launches(const moe_get_shape_t *shape) {
+  const int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  return layout_dispatch_launch_count(layout_sizes(shape));
 }
 
 int moe_combine(const moe_get_shape_t *shape, const uint16_t *expert_out,

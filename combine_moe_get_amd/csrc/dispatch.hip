@@ -22,28 +22,9 @@
 // Loads are ordinary (the row is read once, K stores reuse it from VGPRs);
 // stores are non-temporal: receive rows are written once and read by a later
 // kernel.
-#include "moe_internal.hpp"
+#include "dispatch_dev.hpp"
 
 namespace moe {
-
-__device__ __forceinline__ int sat_code(float p) {
-  float r = __builtin_rintf(p);  // round half to even
-  if (r != r) return 0;          // NaN (0 * inf): code 0
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
-  return (int)r;
-}
-
-__device__ __forceinline__ uint32_t pack_i8x4(int a, int b, int c, int d) {
-  return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
-         ((uint32_t)(d & 0xff) << 24);
-}
-
-__device__ __forceinline__ void unpack8(const u32x4 &v, float *f) {
-  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
-  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
-  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
-  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
-}
 
 // ---- bf16 passthrough --------------------------------------------------------
 // wave gw = (token, slice); slice sl covers 16-byte chunks [64 sl, 64 sl + 64)
@@ -77,58 +58,6 @@ __global__ void __launch_bounds__(256) dispatch_copy_kernel(DispatchArgs a, int 
 // block owns channels [16p, 16p + 16) (chunks 2p and 2p + 1).  One code row per
 // token (no smoothing, or one smooth vector for all experts), stored to every
 // routed copy.
-struct QuantLane {
-  int p, l0, l1;
-  bool has0, has1, wide;
-  __device__ QuantLane(int H) {
-    const int nch = H >> 3;
-    p = threadIdx.x;
-    has0 = 2 * p < nch;
-    has1 = 2 * p + 1 < nch;
-    l0 = has0 ? 2 * p : 0;  // in-bounds chunks for lanes past the row end
-    l1 = has1 ? 2 * p + 1 : 0;
-    wide = (H & 15) == 0;  // 16-byte code stores stay aligned
-  }
-  __device__ void load_scales(const float *s, f32x4 *s4) const {
-    const f32x4 *sp = (const f32x4 *)s;
-    s4[0] = sp[2 * l0];
-    s4[1] = sp[2 * l0 + 1];
-    s4[2] = sp[2 * l1];
-    s4[3] = sp[2 * l1 + 1];
-  }
-  // g = fp32(x) * scales, zero on channels past the row end
-  __device__ void scale16(const float *f, const f32x4 *s4, float *g) const {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const f32x4 &sv = s4[e >> 2];
-      const float sc = (e & 3) == 0 ? sv.x : (e & 3) == 1 ? sv.y : (e & 3) == 2 ? sv.z : sv.w;
-      g[e] = ((e < 8) ? has0 : has1) ? f[e] * sc : 0.0f;
-    }
-  }
-  template <int MODE>
-  __device__ void store_codes(const float *g, float dyn, int8_t *row_base) const {
-    int cd[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) cd[e] = sat_code(MODE == 2 ? g[e] * dyn : g[e]);
-    const u32x2 lo = u32x2{pack_i8x4(cd[0], cd[1], cd[2], cd[3]), pack_i8x4(cd[4], cd[5], cd[6], cd[7])};
-    const u32x2 hi = u32x2{pack_i8x4(cd[8], cd[9], cd[10], cd[11]), pack_i8x4(cd[12], cd[13], cd[14], cd[15])};
-    int8_t *dst = row_base + (size_t)p * 16;
-    if (wide && has1) {
-      __builtin_nontemporal_store((u32x4{lo.x, lo.y, hi.x, hi.y}), (u32x4 *)dst);
-    } else {
-      if (has0) __builtin_nontemporal_store(lo, (u32x2 *)dst);
-      if (has1) __builtin_nontemporal_store(hi, (u32x2 *)(dst + 8));
-    }
-  }
-};
-
-// max over the block of the per-wave maxima in red[0..nw)
-__device__ __forceinline__ float block_max_of(const float *red, int nw) {
-  float m = red[0];
-  for (int w = 1; w < nw; ++w) m = fmaxf(m, red[w]);
-  return m;
-}
-
 template <int MODE>
 __global__ void __launch_bounds__(512) dispatch_quant_kernel(DispatchArgs a) {
   __shared__ float red[8];

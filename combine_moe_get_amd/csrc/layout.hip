@@ -22,7 +22,7 @@
 // All outputs are fully rewritten on every call; the only atomics are LDS
 // integer adds and an OR into the sticky status word, so results are
 // deterministic.
-#include "moe_internal.hpp"
+#include "dispatch_dev.hpp"
 
 namespace moe {
 
@@ -47,6 +47,56 @@ __device__ __forceinline__ void zero_bytes(uint8_t *p, size_t n, int tid, int nt
   const size_t nmid = (n - head) >> 4;
   for (size_t i = tid; i < nmid; i += nthr) mid[i] = u32x4{0u, 0u, 0u, 0u};
   for (size_t i = head + (nmid << 4) + tid; i < n; i += nthr) p[i] = 0;
+}
+
+// Slot-parallel passes over tokens: the lanes of a wave take floor(64 / K) whole
+// tokens, one slot each (lane = g * K + j: token g of the pass, slot j).
+struct SlotLanes {
+  int g, j, per;
+  bool on;         // the lane holds a slot
+  uint64_t group;  // the lanes of the same token
+  __device__ SlotLanes(int K, int lane) {
+    per = 64 / K;
+    g = lane / K;
+    j = lane - g * K;
+    on = g < per;
+    group = on ? (((1ull << K) - 1) << (g * K)) : 0ull;  // K <= 16
+  }
+};
+
+// lanes whose key equals the calling lane's (keys < 2^nbits): AND over the key bits of
+// (ballot or its complement).  Every lane of the wave must call it.
+__device__ __forceinline__ uint64_t match_key(int key, int nbits) {
+  uint64_t peers = ~0ull;
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t bl = ballot(bit);
+    peers &= bit ? bl : ~bl;
+  }
+  return peers;
+}
+
+// own >= 0 is the owner rank of the lane's slot: true for the first slot of its token
+// with that owner (so each (token, rank) pair counts once).  Every lane must call it.
+__device__ __forceinline__ bool first_of_owner(const SlotLanes &sl, int own, int nbits_p, int lane) {
+  const uint64_t peers = match_key(own + 1, nbits_p) & sl.group;
+  return own >= 0 && (peers & ((1ull << lane) - 1ull)) == 0ull;
+}
+
+// Exclusive scan over the W per-wave counters of each expert (cnt[w][e], u16), all loads
+// issued before the first store; returns the expert's chunk total.
+template <int W>
+__device__ __forceinline__ int scan_wave_counts(uint16_t *cnt, int Epad, int e) {
+  int c[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) c[w] = cnt[w * Epad + e];
+  int run = 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    cnt[w * Epad + e] = (uint16_t)run;
+    run += c[w];
+  }
+  return run;
 }
 
 template <int W>
@@ -77,38 +127,28 @@ __global__ void __launch_bounds__(W * 64) layout_count_kernel(LayoutArgs a) {
   zero_bytes(a.itr + (size_t)t0 * P, (size_t)BS * P, tid, W * 64);
   __syncthreads();
 
-  // ---- token phase: owner ranks, specials, bad ids --------------------------
+  // ---- token phase (slot-parallel): owner ranks, specials, bad ids ---------
   bool bad = false;
-  for (int tl = tid; tl < BS; tl += W * 64) {
-    if (!act[tl]) continue;
-    const int t = t0 + tl;
-    const int *tid_ids = ids + tl * K;
-    int own[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      own[j] = -1;
-      if (j < K) {
-        const int id = tid_ids[j];
+  {
+    const SlotLanes sl(K, lane);
+    const int nbp = 32 - __builtin_clz((unsigned)P);
+    for (int tb = wv * sl.per; tb < BS; tb += W * sl.per) {  // uniform per wave
+      const int tl = tb + sl.g;
+      int own = -1;
+      if (sl.on && tl < BS && act[tl]) {
+        const int id = ids[tl * K + sl.j];
         if (id == -1) {
         } else if (id < 0 || (int64_t)id >= a.Etot) {
           bad = true;
         } else if (id >= E) {
           atomicAdd(&spec[id - E], 1);
         } else {
-          own[j] = id / a.L;
+          own = id / a.L;
         }
       }
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (j < K && own[j] >= 0) {
-        bool first = true;
-#pragma unroll
-        for (int j2 = 0; j2 < j; ++j2) first = first && (own[j2] != own[j]);
-        if (first) {
-          a.itr[(size_t)t * P + own[j]] = 1;
-          atomicAdd(&rank_tok[own[j]], 1);
-        }
+      if (first_of_owner(sl, own, nbp, lane)) {
+        a.itr[(size_t)(t0 + tl) * P + own] = 1;
+        atomicAdd(&rank_tok[own], 1);
       }
     }
   }
@@ -142,13 +182,7 @@ __global__ void __launch_bounds__(W * 64) layout_count_kernel(LayoutArgs a) {
 
   // ---- exclusive scan over the waves, per expert ----------------------------
   for (int e = tid; e < E; e += W * 64) {
-    int run = 0;
-#pragma unroll
-    for (int w2 = 0; w2 < W; ++w2) {
-      const int c = cnt[w2 * a.Epad + e];
-      cnt[w2 * a.Epad + e] = (uint16_t)run;
-      run += c;
-    }
+    const int run = scan_wave_counts<W>(cnt, a.Epad, e);
     a.recv_counts[(size_t)e * P + s] = run;
     a.ws_cnt_t[(size_t)s * E + e] = run;
   }
@@ -318,12 +352,20 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
 // with the ballot match and written as final rows.  Workgroup 0 also writes the
 // per-expert / per-rank outputs (it saw every token).  Used while the redundant
 // pass stays small (T * K bounded); larger worlds take the two-launch path.
-template <int W>
-__global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a) {
+//
+// With DM >= 0 the same kernel also dispatches (layout + dispatch in one launch,
+// as the CANN dispatch op returns both): the grid is P x M workgroups, workgroup
+// (s, m) computes chunk s's layout like the others (only m == 0 writes it) and
+// then quantizes / copies tokens [m tpw, m tpw + tpw) of the chunk with the rows
+// it holds in LDS (dispatch_token_block; DM = quant mode, PE = per-expert scales).
+template <int W, int DM, bool PE>
+__global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, DispatchArgs d, int tpw) {
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ int wsum[16];
+  __shared__ float red[2][16];
   constexpr int NT = W * 64;
   const int s = blockIdx.x;
+  const bool writer = blockIdx.y == 0;  // writes the layout outputs of chunk s
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int T = a.T, K = a.K, E = a.E, P = a.P, BS = a.BS, NS = a.NS;
   const int Etot = E + NS;
@@ -341,72 +383,75 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a) {
   int *ids = liml + E;                           // [Spad]
   uint16_t *cnt = (uint16_t *)(ids + a.Spad);    // [W][Epad]
   uint16_t *rk = cnt + W * a.Epad;               // [Spad]
-  uint8_t *act = (uint8_t *)(rk + a.Spad);       // [BS]
+  int *rows = (int *)(rk + a.Spad);              // [Spad] final rows (DM >= 0 only)
+  uint8_t *act = DM >= 0 ? (uint8_t *)(rows + a.Spad) : (uint8_t *)(rk + a.Spad);  // [BS]
+
+  // loads issued before the first barrier, so their latency overlaps the set-up below:
+  // this lane's slot of the first pass over all tokens, and the first token this
+  // workgroup dispatches
+  const SlotLanes sl(K, lane);
+  int pre_id = -1;
+  bool pre_on = false;
+  {
+    const int t = wv * sl.per + sl.g;
+    if (sl.on && t < T) {
+      pre_id = a.topk_idx[(size_t)t * K + sl.j];
+      pre_on = !a.mask || a.mask[t];
+    }
+  }
+  TokenPrefetch pf;
+  const int tl_first = (int)blockIdx.y * tpw;
+  if constexpr (DM >= 0) {
+    if (tl_first < BS) dispatch_prefetch<DM, PE>(d, t0 + tl_first, pf);
+  }
 
   for (int i = tid; i < 2 * Ep2; i += NT) hist_lo[i] = 0;
   for (int i = tid; i < P; i += NT) rtok[i] = 0;
   for (int i = tid; i < W * a.Epad / 2; i += NT) ((uint32_t *)cnt)[i] = 0u;
   for (int i = tid; i < S; i += NT) ids[i] = a.topk_idx[slot0 + i];
   for (int i = tid; i < BS; i += NT) act[i] = a.mask ? a.mask[t0 + i] : (uint8_t)1;
-  zero_bytes(a.itr + (size_t)t0 * P, (size_t)BS * P, tid, NT);
+  if (writer) zero_bytes(a.itr + (size_t)t0 * P, (size_t)BS * P, tid, NT);
   __syncthreads();
+  const bool first = writer && s == 0;  // the workgroup that writes the per-expert / per-rank outputs
 
-  // ---- every token's ids: totals, counts below this rank, distinct tokens per rank ----
+  // ---- every token's ids (slot-parallel): totals, counts below this rank, distinct
+  //      tokens per rank (first workgroup) ------------------------------------------
   bool bad = false;
-  const bool vec4 = (K & 3) == 0 && (((uintptr_t)a.topk_idx) & 15) == 0;
-  for (int t = tid; t < T; t += NT) {
-    if (a.mask && !a.mask[t]) continue;
-    int *h = t < t0 ? hist_lo : hist_hi;
-    const int32_t *tk = a.topk_idx + (size_t)t * K;
-    int idv[16];
-    if (vec4) {  // a token's K ids as 16-byte loads
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (4 * q < K) {
-          const int4 v = ((const int4 *)tk)[q];
-          idv[4 * q] = v.x; idv[4 * q + 1] = v.y; idv[4 * q + 2] = v.z; idv[4 * q + 3] = v.w;
+  {
+    const int nbp = 32 - __builtin_clz((unsigned)P);
+    int it = 0;
+    for (int tb = wv * sl.per; tb < T; tb += W * sl.per, ++it) {  // uniform per wave
+      const int t = tb + sl.g;
+      int id = pre_id;
+      bool on = pre_on;
+      if (it > 0) {
+        id = -1;
+        on = false;
+        if (sl.on && t < T) {
+          id = a.topk_idx[(size_t)t * K + sl.j];
+          on = !a.mask || a.mask[t];
         }
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (j < K) idv[j] = tk[j];
-    }
-    int own[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      own[j] = -1;
-      if (j < K) {
-        const int id = idv[j];
-        if (id == -1) {
-        } else if (id < 0 || id >= Etot) {
+      int own = -1;
+      if (on && id != -1) {
+        if (id < 0 || id >= Etot) {
           bad = true;
         } else {
-          atomicAdd(&h[id], 1);
-          if (s == 0 && id < E) own[j] = id / a.L;
+          atomicAdd(&(t < t0 ? hist_lo : hist_hi)[id], 1);
+          if (id < E) own = id / a.L;
         }
       }
-    }
-    if (s == 0) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (j < K && own[j] >= 0) {
-          bool first = true;
-#pragma unroll
-          for (int j2 = 0; j2 < j; ++j2) first = first && (own[j2] != own[j]);
-          if (first) atomicAdd(&rtok[own[j]], 1);
-        }
+      if (first) {  // uniform per workgroup
+        if (first_of_owner(sl, own, nbp, lane)) atomicAdd(&rtok[own], 1);
       }
     }
   }
 
-  // ---- this chunk: is_token_in_rank rows -------------------------------------
-  for (int tl = tid; tl < BS; tl += NT) {
-    if (!act[tl]) continue;
-    const int *ti = ids + tl * K;
-    for (int j = 0; j < K; ++j) {
-      const int id = ti[j];
-      if (id >= 0 && id < E) a.itr[(size_t)(t0 + tl) * P + id / a.L] = 1;
+  // ---- this chunk: is_token_in_rank rows ------------------------------------------
+  if (writer) {
+    for (int i = tid; i < S; i += NT) {
+      const int id = ids[i];
+      if (id >= 0 && id < E && act[i / K]) a.itr[(size_t)t0 * P + (size_t)(i / K) * P + id / a.L] = 1;
     }
   }
 
@@ -438,14 +483,8 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a) {
 
   // ---- per expert: scan over the waves (chunk-local bases), recv_counts column ---
   for (int e = tid; e < E; e += NT) {
-    int run = 0;
-#pragma unroll
-    for (int w2 = 0; w2 < W; ++w2) {
-      const int c = cnt[w2 * a.Epad + e];
-      cnt[w2 * a.Epad + e] = (uint16_t)run;
-      run += c;
-    }
-    a.recv_counts[(size_t)e * P + s] = run;
+    const int run = scan_wave_counts<W>(cnt, a.Epad, e);
+    if (writer) a.recv_counts[(size_t)e * P + s] = run;
   }
 
   // ---- expert offsets: exclusive scan of the totals (each thread 2 * ceil(E / 2NT) experts) ---
@@ -511,57 +550,95 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a) {
       if (row >= liml[id]) {  // only a token repeating an expert id can overflow its window
         overflow = true;
         row = -1;
-      } else {
+      } else if (writer) {
         a.src_info[row] = (int)(slot0 + i);
       }
     }
-    a.dst_row[slot0 + i] = row;
+    if (writer) a.dst_row[slot0 + i] = row;
+    if constexpr (DM >= 0) rows[i] = row;
   }
-  if (overflow) atomicOr(a.status, (uint32_t)MOE_DEV_STATUS_RANK_OVERFLOW);
+  if (writer && overflow) atomicOr(a.status, (uint32_t)MOE_DEV_STATUS_RANK_OVERFLOW);
 
-  if (s != 0) return;
-  if (bad) atomicOr(a.status, (uint32_t)MOE_DEV_STATUS_BAD_EXPERT_ID);
-  for (int e = tid; e < E; e += NT) {
-    a.cnt[e] = offl[e + 1] - offl[e];
-    a.expert_offsets[e] = offl[e];
+  if (first) {
+    if (bad) atomicOr(a.status, (uint32_t)MOE_DEV_STATUS_BAD_EXPERT_ID);
+    for (int e = tid; e < E; e += NT) {
+      a.cnt[e] = offl[e + 1] - offl[e];
+      a.expert_offsets[e] = offl[e];
+    }
+    if (tid == 0) a.expert_offsets[E] = offl[E];
+    for (int r = tid; r <= P; r += NT) a.rank_offsets[r] = offl[r * a.L];
+    for (int r = tid; r < P; r += NT) a.num_tokens_per_rank[r] = rtok[r];
+    for (int z = tid; z < NS; z += NT) a.special_counts[z] = hist_lo[E + z] + hist_hi[E + z];
   }
-  if (tid == 0) a.expert_offsets[E] = offl[E];
-  for (int r = tid; r <= P; r += NT) a.rank_offsets[r] = offl[r * a.L];
-  for (int r = tid; r < P; r += NT) a.num_tokens_per_rank[r] = rtok[r];
-  for (int z = tid; z < NS; z += NT) a.special_counts[z] = hist_lo[E + z] + hist_hi[E + z];
+
+  if constexpr (DM >= 0) {
+    // ---- dispatch of this workgroup's tokens of the chunk -------------------------
+    __syncthreads();  // rows[] complete
+    int par = 0;
+    const int tl0 = (int)blockIdx.y * tpw;
+    const int tl1 = min(BS, tl0 + tpw);
+    for (int tl = tl0; tl < tl1; ++tl)
+      dispatch_token_block<DM, PE>(d, t0 + tl, rows + tl * K, ids + tl * K, red, par, pf, tl == tl_first);
+  }
 }
 
-size_t layout_fused_lds_bytes(int waves, int E, int NS, int Epad, int Spad, int P, int BS) {
+size_t layout_fused_lds_bytes(int waves, int E, int NS, int Epad, int Spad, int P, int BS, bool rows) {
   const size_t ep2 = (size_t)((E + NS + 1) & ~1);
   return 2 * ep2 * 4 + (size_t)P * 4 + (size_t)(E + 1) * 4 + 2 * (size_t)E * 4 + (size_t)Spad * 4 +
-         (size_t)waves * Epad * 2 + (size_t)Spad * 2 + (size_t)BS;
+         (size_t)waves * Epad * 2 + (size_t)Spad * 2 + (rows ? (size_t)Spad * 4 : 0) + (size_t)BS;
 }
 
 // single launch while each workgroup's pass over every token stays small
-static bool use_fused(const LayoutArgs &a) {
-  const size_t flds = layout_fused_lds_bytes(layout_waves(a.E), a.E, a.NS, a.Epad, a.Spad, a.P, a.BS);
+static bool use_fused(const LayoutArgs &a, bool rows) {
+  const size_t flds = layout_fused_lds_bytes(layout_waves(a.E), a.E, a.NS, a.Epad, a.Spad, a.P, a.BS, rows);
   return (int64_t)a.T * a.K <= kFusedMaxSlots && flds <= kMaxLds;
 }
 
-int layout_launch_count(const LayoutArgs &a) { return use_fused(a) ? 1 : 2; }
+int layout_launch_count(const LayoutArgs &a) { return use_fused(a, false) ? 1 : 2; }
+
+int layout_dispatch_launch_count(const LayoutArgs &a) {
+  if (use_fused(a, true)) return 1;
+  return layout_launch_count(a) + (a.T > 0 ? 1 : 0);
+}
+
+template <int W, int DM, bool PE>
+static hipError_t launch_fused(const LayoutArgs &a, const DispatchArgs &d, hipStream_t stream) {
+  const size_t flds = layout_fused_lds_bytes(W, a.E, a.NS, a.Epad, a.Spad, a.P, a.BS, DM >= 0);
+  // gfx950 has 160 KB of LDS per workgroup; more than 64 KB must be asked for
+  if (flds > 65536) {
+    const hipError_t e = hipFuncSetAttribute((const void *)&layout_fused_kernel<W, DM, PE>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)flds);
+    if (e != hipSuccess) return e;
+  }
+  int tpw = 1, M = 1;
+  if (DM >= 0) {  // about 256 workgroups over the world, at least one token each
+    tpw = (a.T + 255) / 256;
+    if (tpw < 1) tpw = 1;
+    M = (a.BS + tpw - 1) / tpw;
+    if (M < 1) M = 1;
+  }
+  hipLaunchKernelGGL((layout_fused_kernel<W, DM, PE>), dim3((unsigned)a.P, (unsigned)M), dim3(W * 64), flds, stream,
+                     a, d, tpw);
+  return hipGetLastError();
+}
+
+template <int W>
+static hipError_t launch_fused_mode(const LayoutArgs &a, const DispatchArgs &d, int dm, bool pe, hipStream_t st) {
+  switch (dm) {
+    case -1: return launch_fused<W, -1, false>(a, d, st);
+    case 0: return launch_fused<W, 0, false>(a, d, st);
+    case 1: return pe ? launch_fused<W, 1, true>(a, d, st) : launch_fused<W, 1, false>(a, d, st);
+    default: return pe ? launch_fused<W, 2, true>(a, d, st) : launch_fused<W, 2, false>(a, d, st);
+  }
+}
 
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {
   const int W = layout_waves(a.E);
-  const size_t flds = layout_fused_lds_bytes(W, a.E, a.NS, a.Epad, a.Spad, a.P, a.BS);
-  if (use_fused(a)) {
-    const void *fn = W == 16 ? (const void *)&layout_fused_kernel<16> : (const void *)&layout_fused_kernel<8>;
-    if (flds > 65536) {
-      const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)flds);
-      if (e != hipSuccess) return e;
-    }
-    if (W == 16)
-      hipLaunchKernelGGL(layout_fused_kernel<16>, dim3(a.P), dim3(16 * 64), flds, stream, a);
-    else
-      hipLaunchKernelGGL(layout_fused_kernel<8>, dim3(a.P), dim3(8 * 64), flds, stream, a);
-    return hipGetLastError();
+  if (use_fused(a, false)) {
+    const DispatchArgs none{};
+    return W == 16 ? launch_fused_mode<16>(a, none, -1, false, stream) : launch_fused_mode<8>(a, none, -1, false, stream);
   }
   const size_t lds = layout_lds_bytes(W, a.Epad, a.Spad, a.P, a.NS, a.BS);
-  // gfx950 has 160 KB of LDS per workgroup; more than 64 KB must be asked for
   const void *fn = W == 16 ? (const void *)&layout_count_kernel<16> : (const void *)&layout_count_kernel<8>;
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -575,6 +652,17 @@ hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(layout_scan_finalize_kernel, dim3(a.P), dim3(1024), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_layout_dispatch(const LayoutArgs &a, const DispatchArgs &d, int quant_mode, bool per_expert,
+                                  hipStream_t stream) {
+  if (use_fused(a, true)) {
+    return layout_waves(a.E) == 16 ? launch_fused_mode<16>(a, d, quant_mode, per_expert, stream)
+                                   : launch_fused_mode<8>(a, d, quant_mode, per_expert, stream);
+  }
+  const hipError_t e = launch_layout(a, stream);
+  if (e != hipSuccess) return e;
+  return launch_dispatch(d, quant_mode, per_expert, stream);
 }
 
 }  // namespace moe

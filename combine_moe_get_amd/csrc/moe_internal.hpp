@@ -95,6 +95,10 @@ struct CombineArgs {
 
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream);
 int layout_launch_count(const LayoutArgs &a);  // kernels launch_layout runs for these sizes
+// layout and dispatch of the same call (one kernel for small worlds, else the two paths in turn)
+hipError_t launch_layout_dispatch(const LayoutArgs &a, const DispatchArgs &d, int quant_mode, bool per_expert,
+                                  hipStream_t stream);
+int layout_dispatch_launch_count(const LayoutArgs &a);
 hipError_t launch_dispatch(const DispatchArgs &a, int quant_mode, bool per_expert, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
 

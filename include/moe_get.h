@@ -181,6 +181,31 @@ int moe_dispatch(const moe_get_shape_t *shape, int32_t quant_mode, const uint16_
                  const int32_t *topk_idx, const int32_t *dst_row, void *expand_x,
                  float *dynamic_scales, float *expand_weights, void *stream);
 
+/* Layout and dispatch in one call, the way the CANN dispatch operator returns
+ * the routing layout (expert_token_nums, ep_recv_counts, assist_info_for_combine)
+ * together with the dispatched rows (its Prototype and Formula).  Results are
+ * identical, bit for bit, to moe_get_layout_ex(shape, rank_stride, ...)
+ * followed by moe_dispatch(shape, quant_mode, ...) with the same arguments;
+ * argument rules and errors are the union of theirs.  Small worlds (T * K <=
+ * 8192 slots) run as a single kernel -- every workgroup derives its chunk's
+ * rows itself and dispatches a share of the chunk's tokens -- which saves the
+ * launches between layout and dispatch on the decode-sized batches the
+ * low-latency kernels target; larger worlds run the layout kernels, then the
+ * dispatch kernel.  Workspace as for moe_get_layout. */
+int moe_layout_dispatch(const moe_get_shape_t *shape, int64_t rank_stride, int32_t quant_mode,
+                        const int32_t *topk_idx, const uint8_t *x_active_mask, const uint16_t *x,
+                        const float *x_smooth_scale, int32_t smooth_rows, const float *topk_weights,
+                        int32_t *num_tokens_per_expert, int32_t *expert_offsets, int32_t *recv_counts,
+                        int32_t *special_counts, int32_t *num_tokens_per_rank, int32_t *rank_offsets,
+                        uint8_t *is_token_in_rank, int32_t *dst_row, int32_t *src_info, void *expand_x,
+                        float *dynamic_scales, float *expand_weights, uint32_t *status_dev, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* Kernel launches one moe_layout_dispatch call makes for this shape (1 for
+ * T * K <= 8192 slots, else the layout's launches plus one); a negative
+ * MOE_ERR_* for an invalid shape. */
+int moe_layout_dispatch_launches(const moe_get_shape_t *shape);
+
 /* Combine: out[t] = bf16( sum_j w[t,j] * Moe_j(t) ), fp32 accumulation in
  * slot order j = 0..K-1, where Moe_j is
  *   routed expert:   expert_out[dst_row[t, j]]

@@ -3,14 +3,15 @@
  *
  * usage: moe_client DIR
  *
- * DIR/shape.txt holds twelve integers: T H K E P Z C Kc num_max quant_mode
- * has_mask smooth_rows.  The inputs are raw little-endian files in DIR:
+ * DIR/shape.txt holds twelve or thirteen integers: T H K E P Z C Kc num_max
+ * quant_mode has_mask smooth_rows [fused].  The inputs are raw little-endian files in DIR:
  * topk_idx.bin (int32 [T,K]), x.bin (bf16 [T,H]), w.bin (fp32 [T,K]),
  * y.bin (bf16 [rows,H], the expert outputs the combine reads), mask.bin (u8 [T],
  * when has_mask), smooth.bin (fp32 [smooth_rows,H], when smooth_rows > 0) and,
  * when Kc > 0, a1.bin, a2.bin, cv.bin (bf16 [Kc,H]).  The client allocates
  * device memory with the HIP runtime, runs moe_get_layout, moe_dispatch and
- * moe_combine through the C ABI of moe_get.h on the null stream, and writes
+ * moe_combine through the C ABI of moe_get.h on the null stream (with fused
+ * = 1, moe_layout_dispatch in place of the first two), and writes
  * every output next to the inputs (out_*.bin).  Exit status 0 on success.
  */
 #define __HIP_PLATFORM_AMD__ 1
@@ -84,8 +85,8 @@ static void check_moe(int s, const char *what) {
 }
 
 int main(int argc, char **argv) {
-  long v[12];
-  int i, has_mask, quant_mode;
+  long v[13];
+  int i, has_mask, quant_mode, fused;
   int64_t smooth_rows, rows;
   moe_get_shape_t sh;
   FILE *f;
@@ -100,6 +101,7 @@ int main(int argc, char **argv) {
   if (!f) return 1;
   for (i = 0; i < 12; ++i)
     if (fscanf(f, "%ld", &v[i]) != 1) return 1;
+  if (fscanf(f, "%ld", &v[12]) != 1) v[12] = 0;
   fclose(f);
   sh.num_tokens = (int32_t)v[0];
   sh.hidden = (int32_t)v[1];
@@ -113,6 +115,7 @@ int main(int argc, char **argv) {
   quant_mode = (int)v[9];
   has_mask = (int)v[10];
   smooth_rows = v[11];
+  fused = (int)v[12];
 
   if (moe_get_abi_version() != MOE_GET_ABI_VERSION) return 4;
   check_moe(moe_get_check_shape(&sh), "moe_get_check_shape");
@@ -160,20 +163,32 @@ int main(int argc, char **argv) {
     }
     CHECK_HIP(hipMemset(d_status, 0, 4));
 
-    check_moe(moe_get_layout(&sh, (const int32_t *)d_topk, (const uint8_t *)d_mask, (int32_t *)d_cnt,
-                             (int32_t *)d_eoff, (int32_t *)d_recv, (int32_t *)d_spec, (int32_t *)d_ntpr,
-                             (int32_t *)d_roff, (uint8_t *)d_itr, (int32_t *)d_dst, (int32_t *)d_src,
-                             (uint32_t *)d_status, d_ws, wsb, NULL),
-              "moe_get_layout");
+    if (fused) {
+      check_moe(moe_layout_dispatch(&sh, 0, quant_mode, (const int32_t *)d_topk, (const uint8_t *)d_mask,
+                                    (const uint16_t *)d_x, (const float *)d_smooth, (int32_t)smooth_rows,
+                                    (const float *)d_w, (int32_t *)d_cnt, (int32_t *)d_eoff, (int32_t *)d_recv,
+                                    (int32_t *)d_spec, (int32_t *)d_ntpr, (int32_t *)d_roff, (uint8_t *)d_itr,
+                                    (int32_t *)d_dst, (int32_t *)d_src, d_ex,
+                                    quant_mode == MOE_QUANT_DYNAMIC_INT8 ? (float *)d_ds : NULL, (float *)d_ew,
+                                    (uint32_t *)d_status, d_ws, wsb, NULL),
+                "moe_layout_dispatch");
+    } else {
+      check_moe(moe_get_layout(&sh, (const int32_t *)d_topk, (const uint8_t *)d_mask, (int32_t *)d_cnt,
+                               (int32_t *)d_eoff, (int32_t *)d_recv, (int32_t *)d_spec, (int32_t *)d_ntpr,
+                               (int32_t *)d_roff, (uint8_t *)d_itr, (int32_t *)d_dst, (int32_t *)d_src,
+                               (uint32_t *)d_status, d_ws, wsb, NULL),
+                "moe_get_layout");
+      check_moe(moe_dispatch(&sh, quant_mode, (const uint16_t *)d_x, (const float *)d_smooth,
+                             (int32_t)smooth_rows, (const float *)d_w, (const int32_t *)d_topk,
+                             (const int32_t *)d_dst, d_ex, quant_mode == MOE_QUANT_DYNAMIC_INT8 ? (float *)d_ds : NULL,
+                             (float *)d_ew, NULL),
+                "moe_dispatch");
+    }
     CHECK_HIP(hipMemcpy(&n_rows, (int32_t *)d_eoff + E, 4, hipMemcpyDeviceToHost));
     rows = n_rows > 0 ? n_rows : 0;
     y = read_file("y", (size_t)rows * H * 2);
     d_y = dev_buf(y, (size_t)rows * H * 2);
     free(y);
-    check_moe(moe_dispatch(&sh, quant_mode, (const uint16_t *)d_x, (const float *)d_smooth, (int32_t)smooth_rows,
-                           (const float *)d_w, (const int32_t *)d_topk, (const int32_t *)d_dst, d_ex,
-                           quant_mode == MOE_QUANT_DYNAMIC_INT8 ? (float *)d_ds : NULL, (float *)d_ew, NULL),
-              "moe_dispatch");
     check_moe(moe_combine(&sh, (const uint16_t *)d_y, (const int32_t *)d_topk, (const float *)d_w,
                           (const uint8_t *)d_mask, (const int32_t *)d_dst, (const uint16_t *)d_x,
                           (const uint16_t *)d_a1, (const uint16_t *)d_a2, (const uint16_t *)d_cv,
@@ -195,8 +210,8 @@ int main(int argc, char **argv) {
     save("dynamic_scales", d_ds, (size_t)rows * 4);
     save("expand_weights", d_ew, (size_t)rows * 4);
     save("out", d_out, T * H * 2);
-    printf("moe_client ok: T=%zu H=%zu K=%zu E=%zu P=%zu rows=%d quant=%d\n", T, H, K, E, P, n_rows,
-           quant_mode);
+    printf("moe_client ok: T=%zu H=%zu K=%zu E=%zu P=%zu rows=%d quant=%d fused=%d\n", T, H, K, E, P, n_rows,
+           quant_mode, fused);
   }
   return 0;
 }

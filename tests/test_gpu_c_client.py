@@ -34,7 +34,7 @@ def _read(d, name, dtype, shape):
     return a.reshape(shape)
 
 
-def _run(tmp, w, quant_mode, num_max=0, smooth_rows=None):
+def _run(tmp, w, quant_mode, num_max=0, smooth_rows=None, fused=False):
     T, H, K, E, P, Z, C, Kc = (w[k] for k in ("T", "H", "K", "E", "P", "Z", "C", "Kc"))
     osh = oracle.make_shape(T, H, K, E, P, Z, C, Kc, num_max)
     mask = w.get("mask")
@@ -54,7 +54,7 @@ def _run(tmp, w, quant_mode, num_max=0, smooth_rows=None):
     d = str(tmp)
     with open(os.path.join(d, "shape.txt"), "w") as f:
         f.write(" ".join(str(int(v)) for v in (T, H, K, E, P, Z, C, Kc, num_max, quant_mode,
-                                                 mask is not None, srows)) + "\n")
+                                                 mask is not None, srows, fused)) + "\n")
     _write(d, "topk_idx", w["topk_idx"].astype(np.int32))
     _write(d, "x", w["x"])
     _write(d, "w", w["topk_weights"].astype(np.float32))
@@ -68,7 +68,7 @@ def _run(tmp, w, quant_mode, num_max=0, smooth_rows=None):
         _write(d, "a2", w["alpha2"])
         _write(d, "cv", w["const_v"])
     print(f"[c-client] T={T} H={H} K={K} E={E} P={P} Z={Z} C={C} Kc={Kc} quant={quant_mode} "
-          f"smooth_rows={srows} mask={mask is not None}", flush=True)
+          f"smooth_rows={srows} mask={mask is not None} fused={fused}", flush=True)
     r = subprocess.run([_client(), d], capture_output=True, text=True, timeout=90)
     print(r.stdout, r.stderr, flush=True)
     assert r.returncode == 0, r.stderr
@@ -99,10 +99,11 @@ def _run(tmp, w, quant_mode, num_max=0, smooth_rows=None):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("seed,quant_mode", [(3, 0), (5, 1), (8, 2)])
-def test_c_client_fuzz(tmp_path, seed, quant_mode):
+def test_c_client_fuzz(tmp_path, seed, quant_mode, fused):
     w = fuzz_world(seed, Z=1, C=1, Kc=1)
-    _run(tmp_path, w, quant_mode)
+    _run(tmp_path, w, quant_mode, fused=fused)
 
 
 @pytest.mark.gpu
@@ -112,9 +113,10 @@ def test_c_client_per_expert_smooth(tmp_path):
 
 
 @pytest.mark.gpu
-def test_c_client_ll_decode_share(tmp_path):
+@pytest.mark.parametrize("fused", [False, True])
+def test_c_client_ll_decode_share(tmp_path, fused):
     inp = make_inputs(2, seed=1, T=256)
     c = inp["cfg"]
     w = dict(T=c["T"], H=c["H"], K=c["K"], E=c["E"], P=c["P"], Z=0, C=0, Kc=0, x=inp["x"],
              topk_idx=inp["topk_idx"], topk_weights=inp["topk_weights"], smooth=inp["smooth"])
-    _run(tmp_path, w, 2, num_max=c["num_max"])
+    _run(tmp_path, w, 2, num_max=c["num_max"], fused=fused)

@@ -1,0 +1,137 @@
+"""moe_layout_dispatch -- layout and dispatch in one call, a single kernel while
+T * K <= 8192 slots -- against the two separate calls (every output buffer, bit
+for bit) and against the oracle (layout and dispatched rows, bit for bit)."""
+import numpy as np
+import pytest
+import torch
+
+import combine_moe_get_amd as mg
+import oracle
+from combine_moe_get_amd import workloads
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    if t is None:
+        return None
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16)
+    if t.dtype == torch.float32:
+        return t.view(torch.int32)
+    return t
+
+
+def _outs(shape, qm, A, H):
+    T, K, P = shape.num_tokens, shape.topk, shape.num_ranks
+    cap = max(P * A if A > 0 else T * K, 1)
+    lay = mg.alloc_layout(shape, G.DEV, A)
+    for t in lay:
+        t.zero_()
+    ex = torch.zeros((cap, H), dtype=torch.bfloat16 if qm == 0 else torch.int8, device=G.DEV)
+    ds = torch.zeros(cap, dtype=torch.float32, device=G.DEV) if qm == 2 else None
+    ew = torch.zeros(cap, dtype=torch.float32, device=G.DEV)
+    return lay, ex, ds, ew, cap
+
+
+def check_fused(T, H, K, E, P, Z, C, Kc, topk, mask, x, w, qm, smooth, num_max=0, stride=0, label="",
+                expect_launches=None):
+    shape = mg.make_shape(T, H, K, E, P, Z, C, Kc, num_max)
+    A = mg.rank_capacity(shape) if stride == "min" else int(stride)
+    n_launch = mg.layout_dispatch_launches(shape)
+    print(f"[fused] {label} T={T} H={H} K={K} E={E} P={P} Z={Z} C={C} Kc={Kc} qm={qm} "
+          f"smooth_rows={G.smooth_rows_of(smooth, H)} mask={mask is not None} stride={A} launches={n_launch}",
+          flush=True)
+    if expect_launches is not None:
+        assert n_launch == expect_launches
+    tk, mk, xd, wd, sd = G.dev(topk), G.dev(mask), G.dev(x), G.dev(w), G.dev(smooth)
+
+    l1, ex1, ds1, ew1, cap = _outs(shape, qm, A, H)
+    mg.layout(shape, tk, mk, out=l1, rank_stride=A)
+    mg.dispatch(shape, qm, xd, l1.dst_row, sd, wd, tk, ex1, ds1, ew1, rows=cap)
+    l2, ex2, ds2, ew2, _ = _outs(shape, qm, A, H)
+    mg.layout_dispatch(shape, qm, xd, tk, mk, sd, wd, out=l2, expand_x=ex2, dynamic_scales=ds2,
+                       expand_weights=ew2, rank_stride=A)
+    torch.cuda.synchronize()
+    for name, a, b in zip(l1._fields, l1, l2):
+        assert torch.equal(a, b), f"layout output {name} differs from moe_get_layout"
+    assert torch.equal(_bits(ex1), _bits(ex2)), "expand_x differs from moe_dispatch"
+    if qm == 2:
+        assert torch.equal(_bits(ds1), _bits(ds2)), "dynamic_scales differ from moe_dispatch"
+    assert torch.equal(_bits(ew1), _bits(ew2)), "expand_weights differ from moe_dispatch"
+
+    # and against the oracle
+    osh = oracle.make_shape(T, H, K, E, P, Z, C, Kc, num_max)
+    lo = oracle.layout(osh, topk, mask, rank_stride=A)
+    do = oracle.dispatch(osh, qm, x, lo, smooth=smooth, weights=w, topk_idx=topk)
+    g = G.layout_to_numpy(l2, A)
+    o = dict(lo)
+    rows = np.sort(lo["dst_row"][lo["dst_row"] >= 0]).astype(np.int64)
+    if A > 0:
+        g["src_info"] = g["src_info"][rows]
+        o["src_info"] = lo["src_info"][rows]
+    G.assert_layout_equal(g, o)
+    rt = torch.from_numpy(rows).to(G.DEV)
+    gx = G.host_bf16(ex2[rt]) if qm == 0 else ex2[rt].cpu().numpy()
+    assert np.array_equal(gx, do["expand_x"][rows]), "dispatched rows differ from the oracle"
+    if qm == 2:
+        assert np.array_equal(ds2[rt].cpu().numpy().view(np.uint32), do["dynamic_scales"][rows].view(np.uint32))
+    assert np.array_equal(ew2[rt].cpu().numpy(), do["expand_weights"][rows])
+    return n_launch
+
+
+def _fuzz_args(seed):
+    fz = workloads.fuzz_world(seed, p_bad=0.02 if seed % 5 == 4 else 0.0)
+    qm = seed % 3
+    sm = [None, "channel", "expert"][(seed // 3) % 3] if qm else None
+    smooth = None
+    if sm == "channel":
+        smooth = fz["smooth"]
+    elif sm == "expert":
+        f = 0.75 + 0.5 * np.arange(fz["E"], dtype=np.float32)[:, None] / fz["E"]
+        smooth = np.ascontiguousarray(fz["smooth"][None, :] * f, np.float32)
+    stride = "min" if seed % 4 == 3 else 0
+    return fz, qm, smooth, stride
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_fused_fuzz_worlds(seed):
+    fz, qm, smooth, stride = _fuzz_args(seed)
+    check_fused(fz["T"], fz["H"], fz["K"], fz["E"], fz["P"], fz["Z"], fz["C"], fz["Kc"], fz["topk_idx"],
+                fz["mask"], fz["x"], fz["topk_weights"], qm, smooth, stride=stride, label=f"fuzz seed {seed}")
+
+
+@pytest.mark.parametrize("cid,T,P,launches", [(2, 128, 1, 1), (2, 1024, None, 1), (2, None, None, 3),
+                                              (3, 1024, None, 1), (4, 512, None, 1), (5, 1024, None, 1),
+                                              (1, None, None, 1)])
+def test_fused_named_workloads(cid, T, P, launches):
+    inp = workloads.make_inputs(cid, seed=3, T=T, P=P)
+    c = inp["cfg"]
+    check_fused(c["T"], c["H"], c["K"], c["E"], c["P"], c["Z"], c["C"], c["Kc"], inp["topk_idx"], inp["mask"],
+                inp["x"], inp["topk_weights"], c["quant_mode"], inp["smooth"], c["num_max"],
+                label=f"workload {cid} ({c['name']})", expect_launches=launches)
+
+
+@pytest.mark.parametrize("case", ["wide_E", "max_slots", "ragged_H", "max_H", "empty", "per_expert_share"])
+def test_fused_edge_cases(case):
+    r = workloads.rng_for(11, 77, 0)
+    if case == "wide_E":  # E > 1024: 8-wave workgroups
+        T, H, K, E, P = 64, 1024, 16, 2048, 2
+    elif case == "max_slots":  # T * K = 8192 exactly, one rank with 512 tokens
+        T, H, K, E, P = 512, 2048, 16, 64, 1
+    elif case == "ragged_H":
+        T, H, K, E, P = 96, 520, 4, 32, 4
+    elif case == "max_H":
+        T, H, K, E, P = 64, 8192, 8, 64, 8
+    elif case == "empty":
+        T, H, K, E, P = 0, 1024, 4, 16, 4
+    else:
+        T, H, K, E, P = 128, 7168, 8, 256, 1
+    topk = np.argsort(r.random((T, E)), axis=1)[:, :K].astype(np.int32) if T else np.zeros((0, K), np.int32)
+    x = workloads.normal_bf16(r, (T, H))
+    w = r.random((T, K)).astype(np.float32)
+    smooth = r.uniform(0.5, 1.5, (E, H) if case in ("wide_E", "per_expert_share") else H).astype(np.float32)
+    for qm in (0, 1, 2):
+        n = check_fused(T, H, K, E, P, 0, 0, 0, topk, None, x, w, qm, smooth if qm else None, label=case)
+        assert n == 1
