@@ -242,6 +242,15 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int E = a.E, P = a.P, NS = a.NS, K = a.K;
   const int G = E >= 1024 ? 1 : 1024 / E;  // row groups per expert column
+  const int S = a.BS * K;
+  const size_t slot0 = (size_t)s * S;
+  // the thread's first slot of the chunk (local rank and id), loaded now so the latency
+  // overlaps the reduction below
+  int pre_v = -1, pre_e = 0;
+  if (tid < S) {
+    pre_v = a.dst_row[slot0 + tid];
+    pre_e = a.topk_idx[slot0 + tid];
+  }
 
   // partial column sums: virtual thread (e, g) sums rows g, g+G, ... of the count matrix
   for (int v = tid; v < E * G; v += 1024) {
@@ -305,13 +314,11 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
   __syncthreads();
 
   // rows of this chunk's slots
-  const int S = a.BS * K;
-  const size_t slot0 = (size_t)s * S;
   bool overflow = false;
   for (int i = tid; i < S; i += 1024) {
-    const int v = a.dst_row[slot0 + i];
+    const int v = i == tid ? pre_v : a.dst_row[slot0 + i];
     if (v < 0) continue;
-    const int e = a.topk_idx[slot0 + i];
+    const int e = i == tid ? pre_e : a.topk_idx[slot0 + i];
     const int row = basel[e] + v;
     if (row >= liml[e]) {  // only a token repeating an expert id can overflow its window
       overflow = true;
