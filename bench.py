@@ -74,7 +74,8 @@ def source_hash(paths):
 
 KERNEL_SOURCES = {
     "combine": ["combine_moe_get_amd/csrc/combine.hip", "combine_moe_get_amd/csrc/moe_internal.hpp"],
-    "dispatch": ["combine_moe_get_amd/csrc/dispatch.hip", "combine_moe_get_amd/csrc/moe_internal.hpp"],
+    "dispatch": ["combine_moe_get_amd/csrc/dispatch.hip", "combine_moe_get_amd/csrc/dispatch_dev.hpp",
+                 "combine_moe_get_amd/csrc/moe_internal.hpp"],
 }
 
 
