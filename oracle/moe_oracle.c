@@ -45,6 +45,13 @@
  *  R8  the fixed-capacity layout gives rank r the receive window
  *      [r*A, r*A + A) with A >= num_max * ep_world_size * min(L, K) (the
  *      Constraints section's A); its rows keep the compact order.
+ *
+ * Every function is pinned by the tests to something other than itself (hand
+ * cases, the page's routing tables, brute force, exact rational arithmetic,
+ * closed forms).  Parity unpinned against the pages themselves: readings R2
+ * and R3 (no output is printed that would fix the special-id order or the
+ * mask semantics), and the export choices for num_tokens_per_rank (distinct
+ * tokens) and the carried top-k weight; these rest on the readings only.
  */
 #include <math.h>
 #include <stdint.h>
