@@ -299,16 +299,26 @@ def run_dbo(args):
                       "results": results}), flush=True)
 
 
+MALL_BYTES = 256 << 20  # MI355X Infinity Cache
+
+
+def rotation_sets(x_bytes):
+    """Input sets the timed loops cycle through so that no token row is still cached when it is
+    read again: the x rows of all sets together span twice the Infinity Cache.  (With two sets the
+    x rows of both stayed cached between steps -- the other traffic of a step is non-temporal --
+    and dispatch read them from the cache: 47 us instead of 59 us at workload 2.)"""
+    return int(min(12, max(2, -(-2 * MALL_BYTES // max(int(x_bytes), 1)))))
+
+
 def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False):
     """One step benchmark of a workload (tokens / ranks override T and P); returns the JSON
     line without cpu_baseline, and the first input set."""
     import torch
 
     cid = args.workload
-    sets = []
-    for r in range(args.rotate):
-        inp = workloads.make_inputs(cid, seed=args.seed + r, T=tokens, P=ranks)
-        sets.append(inp)
+    first = workloads.make_inputs(cid, seed=args.seed, T=tokens, P=ranks)
+    n_sets = args.rotate if args.rotate else rotation_sets(first["x"].nbytes)
+    sets = [first] + [workloads.make_inputs(cid, seed=args.seed + r, T=tokens, P=ranks) for r in range(1, n_sets)]
     c = sets[0]["cfg"]
     T, H, K, E, P, qm = c["T"], c["H"], c["K"], c["E"], c["P"], c["quant_mode"]
     if args.quant is not None:
@@ -572,7 +582,9 @@ def main():
                     help="override the smooth scales: none, one [H] vector, or [E, H] per expert")
     ap.add_argument("--ranks", type=int, default=None,
                     help="override P; with --tokens equal to one rank's batch this times one rank's share")
-    ap.add_argument("--rotate", type=int, default=2, help="input sets cycled through (defeats cache reuse)")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input sets cycled through; 0 (default): enough that the token rows of all sets "
+                         "span twice the 256 MB Infinity Cache (at most 12)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rank-stride", default="0",
