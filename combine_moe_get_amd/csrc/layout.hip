@@ -7,9 +7,10 @@
 // dispatch_t ...", the masking snippet).  Two launches:
 //
 //  1. count (one workgroup per source rank = one chunk of BS tokens): the
-//     chunk's ids are staged in LDS once; per-wave histograms in LDS are built
-//     with a ballot "match" over the expert-id bits, so a wave ranks 64 slots
-//     in order without atomics; a scan over the waves turns them into
+//     chunk's ids are staged in LDS once; a slot-parallel pass (one lane per
+//     slot) finds owners, specials and bad ids; per-wave histograms in LDS are
+//     built with a ballot "match" over the expert-id bits, so a wave ranks 64
+//     slots in order without atomics; a scan over the waves turns them into
 //     chunk-local stable ranks (kept in dst_row), recv_counts[:, s] (and its
 //     transpose in the workspace), is_token_in_rank rows and per-chunk
 //     rank / special counts.
@@ -18,6 +19,10 @@
 //     totals into offsets and writes dst_row = first row of (s, e) + local
 //     rank and src_info for its chunk; workgroup 0 writes the per-expert and
 //     per-rank outputs.
+//
+// Small worlds (T * K <= 8192 slots) take one launch instead
+// (layout_fused_kernel, below), optionally followed in the same kernel by the
+// dispatch.
 //
 // All outputs are fully rewritten on every call; the only atomics are LDS
 // integer adds and an OR into the sticky status word, so results are
@@ -29,7 +34,7 @@ namespace moe {
 int layout_waves(int E) { return E <= 1024 ? 16 : 8; }
 
 // the single-launch layout re-reads every token's ids in each of the P workgroups; that pass is
-// latency-bound, so it only pays while it is short (one launch saved, ~3 us)
+// latency-bound, so it only pays while it is short (one launch saved)
 static constexpr int64_t kFusedMaxSlots = 8192;  // measured: faster below ~10K slots, slower above
 static constexpr size_t kMaxLds = 160 * 1024;  // gfx950 LDS per workgroup
 
@@ -352,7 +357,7 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
 
 // ---- single-launch layout ---------------------------------------------------
 // One workgroup per source rank s, no communication between workgroups: each
-// first histograms the ids of ALL tokens (token-parallel, LDS integer atomics --
+// first histograms the ids of ALL tokens (slot-parallel, LDS integer atomics --
 // counts do not depend on order), split into tokens of ranks below s (hist_lo)
 // and the rest (hist_hi).  Expert totals are hist_lo + hist_hi, the first row of
 // (s, e) is offset[e] + hist_lo[e]; the chunk's own slots are then ranked in order
