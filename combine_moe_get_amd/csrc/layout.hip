@@ -17,8 +17,9 @@
 //  2. scan + finalize (one workgroup per source rank): each reduces the
 //     [P][E] count matrix with all loads in flight at once, scans the expert
 //     totals into offsets and writes dst_row = first row of (s, e) + local
-//     rank and src_info for its chunk; workgroup 0 writes the per-expert and
-//     per-rank outputs.
+//     rank and src_info for its chunk; workgroup s also writes
+//     num_tokens_per_rank[s] and the totals of special ids s, s + P, ...
+//     (their inputs loaded at the start), workgroup 0 the per-expert outputs.
 //
 // Small worlds (T * K <= 8192 slots) take one launch instead
 // (layout_fused_kernel, below), optionally followed in the same kernel by the
@@ -37,6 +38,7 @@ int layout_waves(int E) { return E <= 1024 ? 16 : 8; }
 // latency-bound, so it only pays while it is short (one launch saved)
 static constexpr int64_t kFusedMaxSlots = 8192;  // measured: faster below ~10K slots, slower above
 static constexpr size_t kMaxLds = 160 * 1024;  // gfx950 LDS per workgroup
+static constexpr int kSpecPerBlock = 8;        // special-id totals one scan workgroup sums from its prefetch
 
 size_t layout_lds_bytes(int waves, int Epad, int Spad, int P, int NS, int BS) {
   return (size_t)Spad * 4 + (size_t)waves * Epad * 2 + (size_t)Spad * 2 + (size_t)P * 4 +
@@ -243,19 +245,29 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
   __shared__ int liml[2048];
   __shared__ int offl[2049];
   __shared__ int wsum[16];
+  __shared__ int acc_rt;             // distinct tokens on rank s, summed over the source chunks
+  __shared__ int acc_sp[kSpecPerBlock];  // special ids s, s + P, ... summed over the source chunks
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int E = a.E, P = a.P, NS = a.NS, K = a.K;
   const int G = E >= 1024 ? 1 : 1024 / E;  // row groups per expert column
   const int S = a.BS * K;
   const size_t slot0 = (size_t)s * S;
-  // the thread's first slot of the chunk (local rank and id), loaded now so the latency
-  // overlaps the reduction below
+  // loads issued now so their latency overlaps the reduction below: the thread's first slot
+  // of the chunk (local rank and id); an element of column s of the per-chunk rank-token
+  // counts; an element of the per-chunk special counts of the ids this workgroup totals
+  // (s + k P, k < kSpecPerBlock, as element (i, k) = (e2 % P, e2 / P))
   int pre_v = -1, pre_e = 0;
   if (tid < S) {
     pre_v = a.dst_row[slot0 + tid];
     pre_e = a.topk_idx[slot0 + tid];
   }
+  const int pre_rt = tid < P ? a.ws_rank_tok[(size_t)tid * P + s] : 0;
+  const int nsp = s < NS ? min(kSpecPerBlock, (NS - s + P - 1) / P) : 0;  // special ids of this workgroup
+  int pre_sp = 0;
+  if (tid < P * nsp) pre_sp = a.ws_special[(size_t)(tid % P) * NS + s + (tid / P) * P];
+  if (tid == 0) acc_rt = 0;
+  if (tid < kSpecPerBlock) acc_sp[tid] = 0;
 
   // partial column sums: virtual thread (e, g) sums rows g, g+G, ... of the count matrix
   for (int v = tid; v < E * G; v += 1024) {
@@ -266,6 +278,12 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
     red_pre[v] = below;
   }
   __syncthreads();
+  if (pre_rt) atomicAdd(&acc_rt, pre_rt);
+  if (pre_sp) atomicAdd(&acc_sp[tid / P], pre_sp);
+  // columns longer than the workgroup (P > 1024) and further special ids (rare)
+  for (int i = tid + 1024; i < P; i += 1024) atomicAdd(&acc_rt, a.ws_rank_tok[(size_t)i * P + s]);
+  for (int e2 = tid + 1024; e2 < P * nsp; e2 += 1024)
+    atomicAdd(&acc_sp[e2 / P], a.ws_special[(size_t)(e2 % P) * NS + s + (e2 / P) * P]);
   for (int e = tid; e < E; e += 1024) {
     int tot = 0, below = 0;
     for (int g = 0; g < G; ++g) {
@@ -335,6 +353,16 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
   }
   if (overflow) atomicOr(a.status, (uint32_t)MOE_DEV_STATUS_RANK_OVERFLOW);
 
+  // per-rank and special totals (accumulated after the first barrier; several barriers since)
+  if (tid == 0) a.num_tokens_per_rank[s] = acc_rt;
+  if (tid < nsp) a.special_counts[s + tid * P] = acc_sp[tid];
+  // special ids beyond what P workgroups of kSpecPerBlock cover (NS > P kSpecPerBlock): summed here
+  for (int z = s + kSpecPerBlock * P + tid * P; z < NS; z += 1024 * P) {
+    int tot = 0, below = 0;
+    column_sums(a.ws_special, NS, z, P, 0, 1, 0, tot, below);
+    a.special_counts[z] = tot;
+  }
+
   if (s != 0) return;
   for (int e = tid; e < E; e += 1024) {
     a.cnt[e] = totl[e];
@@ -342,16 +370,6 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
   }
   if (tid == 0) a.expert_offsets[E] = offl[E];
   for (int r = tid; r <= P; r += 1024) a.rank_offsets[r] = offl[r * a.L];
-  for (int r = tid; r < P; r += 1024) {
-    int tot = 0, below = 0;
-    column_sums(a.ws_rank_tok, P, r, P, 0, 1, 0, tot, below);
-    a.num_tokens_per_rank[r] = tot;
-  }
-  for (int z = tid; z < NS; z += 1024) {
-    int tot = 0, below = 0;
-    column_sums(a.ws_special, NS, z, P, 0, 1, 0, tot, below);
-    a.special_counts[z] = tot;
-  }
 }
 
 

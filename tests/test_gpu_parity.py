@@ -359,6 +359,29 @@ def test_two_launch_layout_for_large_worlds(stride):
     G.assert_layout_equal(g, lo)
 
 
+@pytest.mark.parametrize("P,BS,K,E,Z,C,Kc", [(4, 512, 16, 64, 14, 13, 13),  # 40 special ids over 4 ranks
+                                               (2, 512, 16, 64, 10, 10, 10),  # 30 special ids, 2 ranks
+                                               (2048, 1, 16, 2048, 1, 1, 1),  # more ranks than threads
+                                               (64, 256, 8, 256, 3, 0, 2)])
+def test_two_launch_layout_rank_and_special_totals(P, BS, K, E, Z, C, Kc):
+    # per-rank distinct-token and special-id totals of the two-launch layout are summed by the
+    # workgroup of rank s (special ids s, s + P, ...): many specials per workgroup, P > 1024
+    T = P * BS
+    assert T * K > 8192  # the two-launch path
+    r = np.random.default_rng(P + Z)
+    etot = E + Z + C + Kc
+    topk = r.integers(0, etot, size=(T, K)).astype(np.int32)
+    topk[r.random((T, K)) < 0.05] = -1
+    mask = (r.random(T) < 0.9).astype(np.uint8)
+    shape, osh = G.shapes(T, 64, K, E, P, Z, C, Kc)
+    assert mg.layout_launches(shape) == 2
+    print(f"[case] two-launch totals P={P} BS={BS} K={K} E={E} specials={Z + C + Kc}", flush=True)
+    lo = oracle.layout(osh, topk, mask)
+    lay = mg.layout(shape, G.dev(topk), G.dev(mask))
+    torch.cuda.synchronize()
+    G.assert_layout_equal(G.layout_to_numpy(lay), lo)
+
+
 @pytest.mark.parametrize("qm", [1, 2])
 def test_per_expert_smooth_scales_full_size(qm):
     # the decode workload with [E, H] smooth scales (each copy quantized with its expert's row)
