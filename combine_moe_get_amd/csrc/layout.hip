@@ -300,22 +300,12 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
   const int v0 = e0 < E ? totl[e0] : 0;
   const int v1 = e1 < E ? totl[e1] : 0;
   const int local = v0 + v1;
-  int incl = local;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(incl, o);
-    if (lane >= o) incl += n;
-  }
+  const int incl = wave_inclusive_sum(local);
   if (lane == 63) wsum[wv] = incl;
   __syncthreads();
   if (wv == 0) {
     const int ws = lane < 16 ? wsum[lane] : 0;
-    int wi = ws;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const int n = __shfl_up(wi, o);
-      if (lane >= o) wi += n;
-    }
+    const int wi = wave_inclusive_sum(ws);
     if (lane < 16) wsum[lane] = wi - ws;  // exclusive prefix of the wave totals
   }
   __syncthreads();
@@ -527,22 +517,12 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
       v[u] = e < E ? hist_lo[e] + hist_hi[e] : 0;
       local += v[u];
     }
-    int incl = local;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int n = __shfl_up(incl, o);
-      if (lane >= o) incl += n;
-    }
+    const int incl = wave_inclusive_sum(local);
     if (lane == 63) wsum[wv] = incl;
     __syncthreads();
     if (wv == 0) {
       const int ws = lane < W ? wsum[lane] : 0;
-      int wi = ws;
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const int n = __shfl_up(wi, o);
-        if (lane >= o) wi += n;
-      }
+      const int wi = wave_inclusive_sum(ws);
       if (lane < W) wsum[lane] = wi - ws;
     }
     __syncthreads();

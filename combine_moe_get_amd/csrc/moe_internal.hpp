@@ -37,6 +37,20 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
 extern "C" __device__ float __ockl_wfred_max_f32(float);
 __device__ __forceinline__ float wave_max(float v) { return __ockl_wfred_max_f32(v); }
 
+// inclusive prefix sum over the 64 lanes with DPP moves (no LDS round trips): shifts by
+// 1, 2, 4, 8 lanes inside each row of 16, then lane 15 of rows 0 / 2 into rows 1 / 3 and
+// lane 31 into rows 2 and 3.  A lane whose DPP source is outside its row, or whose row is
+// masked off, reads the `old` operand, 0.  Every lane of the wave must call it.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
 // ---- bf16 <-> fp32 --------------------------------------------------------
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
