@@ -17,8 +17,9 @@
 //    bf16 in, 16 bytes of codes out, so every store instruction of a wave
 //    writes 1 KB contiguous); the dynamic scale needs the row's amax: a wave
 //    max, then a max over the <= 8 waves through LDS.
-//  - int8 with per-expert scales: one workgroup per (token, expert group), the
-//    copies quantized one at a time (see dispatch_quant_expert_kernel).
+//  - int8 with per-expert scales: one workgroup per token (dynamic) or per
+//    (token, expert-id parity) (static), the copies quantized one at a time (see
+//    dispatch_quant_expert_kernel).
 // Loads are ordinary (the row is read once, K stores reuse it from VGPRs);
 // stores are non-temporal: receive rows are written once and read by a later
 // kernel.
@@ -110,18 +111,23 @@ __global__ void __launch_bounds__(512) dispatch_quant_kernel(DispatchArgs a) {
 // so where they are served from decides the speed.  Block b handles token b / G
 // and only the copies whose expert id e has e % G == b % G; workgroups are placed
 // on the 8 XCDs round-robin by block id, so with G = 2 each XCD's L2 sees half of
-// the scale rows.  (G = 8, one eighth per XCD, measured slower on gfx950: the
-// token row is then fetched by every XCD and many blocks have little work.)
+// the scale rows.  Measured on gfx950 with every input read from HBM: G = 2 is
+// best for static codes (109 us against 117 for G = 1, 112 for G = 4 at T=4096,
+// H=7168, top-8); with the dynamic scale's block-wide amax per copy, G = 1 is
+// (121 against 127 for G = 2) -- splitting a token's copies adds barriers to fewer
+// copies per block.  G = 8 loses in both (the token row is fetched by every XCD).
 // Copies are quantized one at a time with the codes kept in registers across the
 // block-wide amax, so each scale row is read once per copy.
-constexpr int kExpertGroups = 2;
+template <int MODE>
+constexpr int expert_groups() { return MODE == 1 ? 2 : 1; }
 
 template <int MODE>
 __global__ void __launch_bounds__(512) dispatch_quant_expert_kernel(DispatchArgs a) {
+  constexpr int G = expert_groups<MODE>();
   __shared__ float red[2][8];  // alternated per copy: one barrier per copy suffices
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
-  const int t = blockIdx.x / kExpertGroups, grp = blockIdx.x % kExpertGroups;
+  const int t = blockIdx.x / G, grp = blockIdx.x % G;
   const int K = a.K, H = a.H;
 
   int myrow = -1, myid = 0;
@@ -129,7 +135,7 @@ __global__ void __launch_bounds__(512) dispatch_quant_expert_kernel(DispatchArgs
     myrow = a.dst_row[(size_t)t * K + lane];
     myid = a.topk_idx[(size_t)t * K + lane];
   }
-  const bool mine = myrow >= 0 && myid % kExpertGroups == grp;  // routed rows have 0 <= id < E
+  const bool mine = myrow >= 0 && myid % G == grp;  // routed rows have 0 <= id < E
   uint64_t sel = ballot(mine);
   if (sel == 0ull) return;  // same for every wave of the block
 
@@ -178,15 +184,16 @@ hipError_t launch_dispatch(const DispatchArgs &a, int quant_mode, bool per_exper
   }
   const int pairs = (nch + 1) / 2;  // <= 512 for H <= 8192
   const dim3 blk(64 * ((pairs + 63) / 64));
-  const dim3 g((unsigned)a.T), ge((unsigned)((int64_t)a.T * kExpertGroups));
+  const dim3 g((unsigned)a.T);
+  const dim3 ge1((unsigned)((int64_t)a.T * expert_groups<1>())), ge2((unsigned)((int64_t)a.T * expert_groups<2>()));
   if (quant_mode == 1 && !per_expert)
     hipLaunchKernelGGL((dispatch_quant_kernel<1>), g, blk, 0, stream, a);
   else if (quant_mode == 1)
-    hipLaunchKernelGGL((dispatch_quant_expert_kernel<1>), ge, blk, 0, stream, a);
+    hipLaunchKernelGGL((dispatch_quant_expert_kernel<1>), ge1, blk, 0, stream, a);
   else if (!per_expert)
     hipLaunchKernelGGL((dispatch_quant_kernel<2>), g, blk, 0, stream, a);
   else
-    hipLaunchKernelGGL((dispatch_quant_expert_kernel<2>), ge, blk, 0, stream, a);
+    hipLaunchKernelGGL((dispatch_quant_expert_kernel<2>), ge2, blk, 0, stream, a);
   return hipGetLastError();
 }
 
