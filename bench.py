@@ -93,6 +93,37 @@ def counter_traffic(kernel, workload_name):
     return float(m_b.group(1))
 
 
+def hbm_probe(dev, nbytes=2 << 30, reps=5):
+    """What library streaming kernels reach on this GPU, on a buffer 8x the Infinity Cache:
+    a fill (pure write, sequential addresses) and a device-to-device copy (read + write).
+    Context for the roofline, which is quoted against the published 8 TB/s."""
+    import torch
+
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    half = nbytes // 2
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return float(np.median(ts))
+
+    t_w = timed(lambda: buf.fill_(1))
+    t_c = timed(lambda: buf[:half].copy_(buf[half:]))
+    del buf
+    torch.cuda.empty_cache()
+    return dict(write_GBps=round(nbytes / t_w / 1e9, 1), copy_rw_GBps=round(2 * half / t_c / 1e9, 1),
+                buffer_bytes=nbytes,
+                kernels="torch fill_ (its vectorized elementwise kernel) / copy_ (hipMemcpy device to device)")
+
+
 def cpu_baseline(inp, target_seconds):
     """The oracle, as it stands (single-threaded C), timed on this host over whole
     layout + dispatch + combine passes of the same workload."""
@@ -598,6 +629,8 @@ def main():
     ap.add_argument("--dbo-f", default="256,512,2048", help="expert intermediate sizes F for --dbo")
     ap.add_argument("--dbo-comm-cus", default="0",
                     help="CUs given to the data-movement stream in --dbo (0: no split; a split needs CU-masked streams)")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the HBM probe (fill and copy of a 2 GiB buffer with library kernels)")
     ap.add_argument("--no-share", action="store_true",
                     help="skip the extra measurement of one rank's share (T = BS, P = 1)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -637,6 +670,8 @@ def main():
             in_step_us_median={k: v["in_step_us_median"] for k, v in sh["kernels"].items()},
             layout_launches=sh["kernels"]["layout"]["launches"],
             fused_layout_dispatch=sh.get("fused_layout_dispatch"))
+    if not args.no_probe:
+        line["hbm_probe"] = hbm_probe(dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp0, args.cpu_seconds)
     print(json.dumps(line), flush=True)
