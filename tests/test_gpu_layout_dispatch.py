@@ -135,3 +135,67 @@ def test_fused_edge_cases(case):
     for qm in (0, 1, 2):
         n = check_fused(T, H, K, E, P, 0, 0, 0, topk, None, x, w, qm, smooth if qm else None, label=case)
         assert n == 1
+
+
+@pytest.mark.parametrize("T", [128, 4096])  # the single kernel, and the layout kernels + dispatch
+def test_fused_graph_replays_match_eager(T):
+    # moe_layout_dispatch captured once and replayed several times with eager work and
+    # synchronizations between replays; every replay must equal the eager result bit for bit
+    inp = workloads.make_inputs(2, seed=6, T=T, P=None if T == 4096 else 1)
+    c = inp["cfg"]
+    shape = mg.make_shape(c["T"], c["H"], c["K"], c["E"], c["P"], num_max=c["num_max"])
+    print(f"[fused graph] T={c['T']} P={c['P']} launches={mg.layout_dispatch_launches(shape)}", flush=True)
+    tk, xd, sd, wd = G.dev(inp["topk_idx"]), G.dev(inp["x"]), G.dev(inp["smooth"]), G.dev(inp["topk_weights"])
+    lay, ex, ds, ew, cap = _outs(shape, 2, 0, c["H"])
+    call = mg.prepare_layout_dispatch(shape, 2, xd, tk, None, sd, wd, out=lay, expand_x=ex, dynamic_scales=ds,
+                                      expand_weights=ew)
+    call()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (lay.dst_row, lay.src_info, lay.expert_offsets, lay.is_token_in_rank, ex, ds, ew)]
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        call(torch.cuda.current_stream())
+    for rep in range(3):
+        lay.dst_row.fill_(-7)
+        ex.zero_()
+        ds.zero_()
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        got = (lay.dst_row, lay.src_info, lay.expert_offsets, lay.is_token_in_rank, ex, ds, ew)
+        for a, b in zip(got, ref):
+            assert torch.equal(_bits(a), _bits(b)), f"replay {rep} differs"
+        call()  # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_two_streams_two_worlds():
+    # two independent worlds (own buffers and workspaces) on two streams at once; each must
+    # equal its own single-stream result
+    worlds = []
+    for seed in (21, 22):
+        fz = workloads.fuzz_world(seed, T=96, P=4, H=1024, K=4, E=16, Z=1, C=1, Kc=0)
+        worlds.append(fz)
+    shapes, calls, outs = [], [], []
+    for fz in worlds:
+        shape = mg.make_shape(fz["T"], fz["H"], fz["K"], fz["E"], fz["P"], fz["Z"], fz["C"], fz["Kc"])
+        lay, ex, ds, ew, cap = _outs(shape, 2, 0, fz["H"])
+        call = mg.prepare_layout_dispatch(shape, 2, G.dev(fz["x"]), G.dev(fz["topk_idx"]), G.dev(fz["mask"]),
+                                          G.dev(fz["smooth"]), G.dev(fz["topk_weights"]), out=lay, expand_x=ex,
+                                          dynamic_scales=ds, expand_weights=ew)
+        shapes.append(shape)
+        calls.append(call)
+        outs.append((lay, ex, ds, ew))
+    refs = []
+    for call, (lay, ex, ds, ew) in zip(calls, outs):
+        call()
+        torch.cuda.synchronize()
+        refs.append([t.clone() for t in (*lay, ex, ds, ew)])
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for _ in range(5):
+        for call, st in zip(calls, streams):
+            call(st)
+    torch.cuda.synchronize()
+    for (lay, ex, ds, ew), ref in zip(outs, refs):
+        for a, b in zip((*lay, ex, ds, ew), ref):
+            assert torch.equal(_bits(a), _bits(b))
