@@ -36,15 +36,17 @@ __global__ void __launch_bounds__(256) dispatch_copy_kernel(DispatchArgs a, int 
   if (t >= a.T) return;  // whole wave
   const int K = a.K, H = a.H, nch = H >> 3;
 
+  // the slice is requested together with the slot rows (not after them): one load latency
+  // less per wave, at the price of reading the slice of a token with no routed copy
   int myrow = -1;
   if (lane < K) myrow = a.dst_row[(size_t)t * K + lane];
+  const int c = lane + 64 * sl;
+  u32x4 v = u32x4{0u, 0u, 0u, 0u};
+  if (c < nch) v = ((const u32x4 *)(a.x + (size_t)t * H))[c];
   uint64_t valid = ballot(myrow >= 0);
   if (valid == 0ull) return;  // masked token, or only special / dropped slots
   const bool write_w = sl == 0 && myrow >= 0 && a.expand_w;
 
-  const int c = lane + 64 * sl;
-  u32x4 v = u32x4{0u, 0u, 0u, 0u};
-  if (c < nch) v = ((const u32x4 *)(a.x + (size_t)t * H))[c];
   while (valid) {
     const int j = __builtin_ctzll(valid);
     valid &= valid - 1;
@@ -67,18 +69,20 @@ __global__ void __launch_bounds__(512) dispatch_quant_kernel(DispatchArgs a) {
   const int t = blockIdx.x;
   const int K = a.K, H = a.H;
 
+  // every load of the lane is issued before the first use: slot rows, row chunks, scales.
+  // The row is requested before the slot rows are known (one load latency less per
+  // token; a token with no routed copy has its row read for nothing).
   int myrow = -1;
   if (lane < K) myrow = a.dst_row[(size_t)t * K + lane];
-  uint64_t valid = ballot(myrow >= 0);
-  if (valid == 0ull) return;  // same for every wave of the block: no barrier is skipped
-
   const QuantLane q(H);
-  // every load of the lane is issued before the first use: row chunks, then scales
   const u32x4 *xr = (const u32x4 *)(a.x + (size_t)t * H);
   const u32x4 v0 = xr[q.l0], v1 = xr[q.l1];
   f32x4 s4[4] = {f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f},
                  f32x4{1.f, 1.f, 1.f, 1.f}};
   if (a.smooth) q.load_scales(a.smooth, s4);
+  uint64_t valid = ballot(myrow >= 0);
+  if (valid == 0ull) return;  // same for every wave of the block: no barrier is skipped
+
   float f[16], g[16];
   unpack8(v0, f);
   unpack8(v1, f + 8);
@@ -135,13 +139,13 @@ __global__ void __launch_bounds__(512) dispatch_quant_expert_kernel(DispatchArgs
     myrow = a.dst_row[(size_t)t * K + lane];
     myid = a.topk_idx[(size_t)t * K + lane];
   }
+  const QuantLane q(H);  // the row is requested with the slots, before they are known
+  const u32x4 *xr = (const u32x4 *)(a.x + (size_t)t * H);
+  const u32x4 v0 = xr[q.l0], v1 = xr[q.l1];
   const bool mine = myrow >= 0 && myid % G == grp;  // routed rows have 0 <= id < E
   uint64_t sel = ballot(mine);
   if (sel == 0ull) return;  // same for every wave of the block
 
-  const QuantLane q(H);
-  const u32x4 *xr = (const u32x4 *)(a.x + (size_t)t * H);
-  const u32x4 v0 = xr[q.l0], v1 = xr[q.l1];
   if (wv == 0 && mine && a.expand_w) a.expand_w[myrow] = a.w ? a.w[(size_t)t * K + lane] : 1.0f;
   float f[16];
   unpack8(v0, f);
