@@ -80,6 +80,7 @@ struct LayoutArgs {
   int32_t *ws_cnt_t;     // [P][E]  routed copies of expert e sent by rank s
   int32_t *ws_rank_tok;  // [P][P]  per source rank: tokens with a copy on rank r
   int32_t *ws_special;   // [P][NS] per source rank: special slots per id
+  int32_t mt;            // 64-bit words per wave of the count kernel's LDS match tables; set by the launcher
 };
 
 struct DispatchArgs {
@@ -118,6 +119,6 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
 
 // LDS bytes of the layout count kernel and its waves per block
 int layout_waves(int E);
-size_t layout_lds_bytes(int waves, int Epad, int Spad, int P, int NS, int BS);
+size_t layout_lds_bytes(int waves, int Epad, int Spad, int P, int NS, int BS, int mt);
 
 }  // namespace moe
