@@ -362,10 +362,20 @@ def test_two_launch_layout_for_large_worlds(stride):
 @pytest.mark.parametrize("P,BS,K,E,Z,C,Kc", [(4, 512, 16, 64, 14, 13, 13),  # 40 special ids over 4 ranks
                                                (2, 512, 16, 64, 10, 10, 10),  # 30 special ids, 2 ranks
                                                (2048, 1, 16, 2048, 1, 1, 1),  # more ranks than threads
-                                               (64, 256, 8, 256, 3, 0, 2)])
+                                               (64, 256, 8, 256, 3, 0, 2),
+                                               # count-kernel variants for chunks above one 64-slot group
+                                               # per wave: 8 waves with LDS match tables (E > 1024),
+                                               (4, 512, 8, 1280, 0, 0, 0),
+                                               # 16 waves whose tables do not fit (ballot match),
+                                               (4, 512, 8, 1024, 0, 0, 0),
+                                               # 16 waves with tables at 8192 slots per chunk,
+                                               (2, 512, 16, 512, 0, 0, 0),
+                                               # an odd top-k with special ids
+                                               (8, 256, 6, 96, 2, 1, 1)])
 def test_two_launch_layout_rank_and_special_totals(P, BS, K, E, Z, C, Kc):
     # per-rank distinct-token and special-id totals of the two-launch layout are summed by the
-    # workgroup of rank s (special ids s, s + P, ...): many specials per workgroup, P > 1024
+    # workgroup of rank s (special ids s, s + P, ...): many specials per workgroup, P > 1024;
+    # large chunks take the count kernel's LDS-table match where its tables fit
     T = P * BS
     assert T * K > 8192  # the two-launch path
     r = np.random.default_rng(P + Z)
