@@ -9,8 +9,9 @@
 //  1. count (one workgroup per source rank = one chunk of BS tokens): the
 //     chunk's ids are staged in LDS once; a slot-parallel pass (one lane per
 //     slot) finds owners, specials and bad ids; per-wave histograms in LDS are
-//     built with a ballot "match" over the expert-id bits, so a wave ranks 64
-//     slots in order without atomics; a scan over the waves turns them into
+//     built with a "match" of the 64 slots of a wave by expert id (ballots
+//     over the id bits, or for large chunks per-wave LDS tables of lane
+//     masks), so a wave ranks 64 slots in order; a scan over the waves turns them into
 //     chunk-local stable ranks (kept in dst_row), recv_counts[:, s] (and its
 //     transpose in the workspace), is_token_in_rank rows and per-chunk
 //     rank / special counts.
@@ -26,7 +27,8 @@
 // dispatch.
 //
 // All outputs are fully rewritten on every call; the only atomics are LDS
-// integer adds and an OR into the sticky status word, so results are
+// integer adds, LDS ORs of lane masks (the match tables) and an OR into the
+// sticky status word, none of which decides an order, so results are
 // deterministic.
 #include "dispatch_dev.hpp"
 
