@@ -47,18 +47,20 @@ int check_shape(const moe_get_shape_t *s) {
   return MOE_OK;
 }
 
-// workspace: [P][E] per-chunk expert counts | [P][P] per-chunk rank tokens | [P][NS] per-chunk specials | status word
+// workspace: [P m][E] per-sub-chunk expert counts | [P m][P] per-sub-chunk rank tokens |
+// [P m][NS] per-sub-chunk specials | status word (m: sub-chunks per source rank)
 struct WsLayout {
   size_t base, rank_tok, special, status, total;
 };
 
 WsLayout ws_layout(const moe_get_shape_t *s) {
   const size_t P = s->num_ranks, E = s->num_experts, NS = n_special(s);
+  const size_t Pv = P * (size_t)layout_subchunks(s->num_tokens / s->num_ranks, s->num_experts, s->num_ranks);
   WsLayout w;
   w.base = 0;
-  w.rank_tok = w.base + align_up(P * E * 4);
-  w.special = w.rank_tok + align_up(P * P * 4);
-  w.status = w.special + align_up(P * (NS > 0 ? NS : 1) * 4);
+  w.rank_tok = w.base + align_up(Pv * E * 4);
+  w.special = w.rank_tok + align_up(Pv * P * 4);
+  w.status = w.special + align_up(Pv * (NS > 0 ? NS : 1) * 4);
   w.total = w.status + kAlign;
   return w;
 }
@@ -113,6 +115,10 @@ static LayoutArgs layout_sizes(const moe_get_shape_t *shape) {
   a.Epad = E + (E & 1);
   const int S = a.BS * K;
   a.Spad = S + (S & 1);
+  a.m = layout_subchunks(a.BS, E, P);
+  a.BSv = a.BS > 0 ? (a.BS + a.m - 1) / a.m : 1;
+  const int Sv = a.BSv * K;
+  a.Svpad = Sv + (Sv & 1);
   a.Etot = (int64_t)E + NS;
   return a;
 }

@@ -39,6 +39,7 @@ int layout_waves(int E) { return E <= 1024 ? 16 : 8; }
 // the single-launch layout re-reads every token's ids in each of the P workgroups; that pass is
 // latency-bound, so it only pays while it is short (one launch saved)
 static constexpr int64_t kFusedMaxSlots = 8192;  // measured: faster below ~10K slots, slower above
+static constexpr int kFusedMaxChunk = 384;         // tokens per source rank (see use_fused)
 static constexpr size_t kMaxLds = 160 * 1024;  // gfx950 LDS per workgroup
 static constexpr int kSpecPerBlock = 8;        // special-id totals one scan workgroup sums from its prefetch
 
@@ -141,26 +142,34 @@ __device__ __forceinline__ int scan_wave_counts(uint16_t *cnt, int Epad, int e) 
 // tables (a.mt words per wave) instead of ballots.  Measured on gfx950: at 4096 slots per
 // chunk (T=8192, 16 ranks) the count kernel takes 9.6 instead of 10.8 us; at 1024 slots the
 // ballot version is faster.
-template <int W, bool BIG>
+//
+// Workgroup v counts sub-chunk v = s m + q: tokens [q BSv, q BSv + nt) of source rank s's
+// chunk (m = 1 and BSv = BS unless chunks of more than 128 tokens are split, so that more
+// workgroups share the latency-bound passes); ranks are local to the sub-chunk and its
+// counts go to row v of the workspace matrices, which the scan kernel combines.
+template <int W, bool BIG, bool SUBS>
 __global__ void __launch_bounds__(W * 64) layout_count_kernel(LayoutArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
-  const int s = blockIdx.x;
+  const int v = blockIdx.x;
+  const int s = SUBS ? v / a.m : v, q = v - s * a.m;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  const int K = a.K, E = a.E, P = a.P, BS = a.BS, NS = a.NS;
-  const int S = BS * K;
-  const int t0 = s * BS;
+  const int K = a.K, E = a.E, P = a.P, NS = a.NS;
+  const int tq = q * a.BSv;                   // first token of the sub-chunk inside the chunk
+  const int nt = min(a.BS, tq + a.BSv) - tq;  // its tokens (at least one)
+  const int S = nt * K;
+  const int t0 = s * a.BS + tq;
   const size_t slot0 = (size_t)t0 * K;
 
   const int mt = BIG ? a.mt : 0;
   uint64_t *mtab = (uint64_t *)lds + (size_t)wv * mt;  // [W][mt] match tables (BIG)
-  int *ids = (int *)(lds + (size_t)W * mt * 8);        // [Spad] the chunk's expert ids
-  uint16_t *cnt = (uint16_t *)(ids + a.Spad);  // [W][Epad] per-wave running counts
-  uint16_t *rk = cnt + W * a.Epad;             // [Spad] rank of a slot inside its wave segment
-  int *rank_tok = (int *)(rk + a.Spad);        // [P]
-  int *spec = rank_tok + P;                    // [NS]
-  uint8_t *act = (uint8_t *)(spec + NS);       // [BS] token active flags
+  int *ids = (int *)(lds + (size_t)W * mt * 8);        // [Svpad] the sub-chunk's expert ids
+  uint16_t *cnt = (uint16_t *)(ids + a.Svpad);  // [W][Epad] per-wave running counts
+  uint16_t *rk = cnt + W * a.Epad;              // [Svpad] rank of a slot inside its wave segment
+  int *rank_tok = (int *)(rk + a.Svpad);        // [P]
+  int *spec = rank_tok + P;                     // [NS]
+  uint8_t *act = (uint8_t *)(spec + NS);        // [BSv] token active flags
 
   // one coalesced pass over the chunk's ids and mask; everything after reads LDS
   if constexpr (BIG) {  // every load issued before the first LDS store (S <= 512 * 16)
@@ -180,11 +189,11 @@ __global__ void __launch_bounds__(W * 64) layout_count_kernel(LayoutArgs a) {
   } else {
     for (int i = tid; i < S; i += W * 64) ids[i] = a.topk_idx[slot0 + i];
   }
-  for (int i = tid; i < BS; i += W * 64) act[i] = a.mask ? a.mask[t0 + i] : (uint8_t)1;
+  for (int i = tid; i < nt; i += W * 64) act[i] = a.mask ? a.mask[t0 + i] : (uint8_t)1;
   for (int i = tid; i < W * a.Epad / 2; i += W * 64) ((uint32_t *)cnt)[i] = 0u;
   for (int i = tid; i < P; i += W * 64) rank_tok[i] = 0;
   for (int i = tid; i < NS; i += W * 64) spec[i] = 0;
-  zero_bytes(a.itr + (size_t)t0 * P, (size_t)BS * P, tid, W * 64);
+  zero_bytes(a.itr + (size_t)t0 * P, (size_t)nt * P, tid, W * 64);
   __syncthreads();
 
   // ---- token phase (slot-parallel): owner ranks, specials, bad ids ---------
@@ -192,10 +201,10 @@ __global__ void __launch_bounds__(W * 64) layout_count_kernel(LayoutArgs a) {
   {
     const SlotLanes sl(K, lane);
     const int nbp = 32 - __builtin_clz((unsigned)P);
-    for (int tb = wv * sl.per; tb < BS; tb += W * sl.per) {  // uniform per wave
+    for (int tb = wv * sl.per; tb < nt; tb += W * sl.per) {  // uniform per wave
       const int tl = tb + sl.g;
       int own = -1;
-      if (sl.on && tl < BS && act[tl]) {
+      if (sl.on && tl < nt && act[tl]) {
         const int id = ids[tl * K + sl.j];
         if (id == -1) {
         } else if (id < 0 || (int64_t)id >= a.Etot) {
@@ -238,23 +247,23 @@ __global__ void __launch_bounds__(W * 64) layout_count_kernel(LayoutArgs a) {
   // ---- exclusive scan over the waves, per expert ----------------------------
   for (int e = tid; e < E; e += W * 64) {
     const int run = scan_wave_counts<W>(cnt, a.Epad, e);
-    a.recv_counts[(size_t)e * P + s] = run;
-    a.ws_cnt_t[(size_t)s * E + e] = run;
+    if constexpr (!SUBS) a.recv_counts[(size_t)e * P + s] = run;  // split chunks: the scan kernel sums
+    a.ws_cnt_t[(size_t)v * E + e] = run;
   }
   __syncthreads();
 
-  // ---- chunk-local stable rank of every slot (made global by the next kernel) ---
+  // ---- sub-chunk-local stable rank of every slot (made global by the next kernel) ---
   for (int base = beg; base < end; base += 64) {
     const int i = base + lane;
     if (i < end) {
       const int id = ids[i];
-      int v = -1;
-      if (act[i / K] && id >= 0 && id < E) v = (int)mycnt[id] + (int)rk[i];
-      a.dst_row[slot0 + i] = v;
+      int r = -1;
+      if (act[i / K] && id >= 0 && id < E) r = (int)mycnt[id] + (int)rk[i];
+      a.dst_row[slot0 + i] = r;
     }
   }
-  for (int r = tid; r < P; r += W * 64) a.ws_rank_tok[(size_t)s * P + r] = rank_tok[r];
-  for (int z = tid; z < NS; z += W * 64) a.ws_special[(size_t)s * NS + z] = spec[z];
+  for (int r = tid; r < P; r += W * 64) a.ws_rank_tok[(size_t)v * P + r] = rank_tok[r];
+  for (int z = tid; z < NS; z += W * 64) a.ws_special[(size_t)v * NS + z] = spec[z];
   if (bad) atomicOr(a.status, (uint32_t)MOE_DEV_STATUS_BAD_EXPERT_ID);
 }
 
@@ -281,16 +290,18 @@ __device__ __forceinline__ void column_sums(const int32_t *m, int ld, int col, i
   }
 }
 
-// One workgroup of 1024 threads per source rank s.  Every workgroup reduces the [P][E]
+// One workgroup of 1024 threads per source rank s.  Every workgroup reduces the [P m][E]
 // count matrix (expert totals and the part sent by ranks below s), scans the totals into
-// expert offsets, and turns its own chunk's local ranks into rows; workgroup 0 also
-// writes the per-expert and per-rank outputs.  E <= 2048.
+// expert offsets, and turns its own chunk's sub-chunk ranks into rows (adding the counts
+// of the chunk's earlier sub-chunks); workgroup 0 also writes the per-expert and per-rank
+// outputs.  E <= 2048, m <= 4 and m E <= 4096.
 // SPT: slots per thread loaded at the start (ceil(S / 1024) <= SPT, S <= 8192); with SPT = 1
 // the slots past the first 1024 are loaded in the last loop.
-template <int SPT>
+template <int SPT, bool SUBS>
 __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a) {
-  __shared__ int red_tot[2048];
-  __shared__ int red_pre[2048];
+  __shared__ int red[2 * 2048];  // partial column sums; later the sub-chunk bases
+  int *red_tot = red, *red_pre = red + 2048;
+  int *subb = red;               // [m - 1][E]: first row of (sub-chunk q >= 1, e) past the chunk's
   __shared__ int totl[2048];
   __shared__ int basel[2048];
   __shared__ int liml[2048];
@@ -301,13 +312,23 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int E = a.E, P = a.P, NS = a.NS, K = a.K;
+  const int m = SUBS ? a.m : 1, Pv = P * m;  // sub-chunks per chunk; rows of the workspace matrices
   const int G = E >= 1024 ? 1 : 1024 / E;  // row groups per expert column
   const int S = a.BS * K;
   const size_t slot0 = (size_t)s * S;
   // loads issued now so their latency overlaps the reduction below: the thread's first SPT
-  // slots of the chunk (local rank and id); an element of column s of the per-chunk
-  // rank-token counts; an element of the per-chunk special counts of the ids this
-  // workgroup totals (s + k P, k < kSpecPerBlock, as element (i, k) = (e2 % P, e2 / P))
+  // slots of the chunk (sub-chunk rank and id); the counts of this chunk's sub-chunks for
+  // experts tid and tid + 1024; an element of column s of the per-sub-chunk rank-token
+  // counts; an element of the per-sub-chunk special counts of the ids this workgroup
+  // totals (s + k P, k < kSpecPerBlock, as element (i, k) = (e2 % Pv, e2 / Pv))
+  int sub[2][4];  // m <= 4
+  if constexpr (SUBS) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        sub[h][qq] = (qq < m && tid + 1024 * h < E) ? a.ws_cnt_t[(size_t)(s * m + qq) * E + tid + 1024 * h] : 0;
+  }
   int pre_v[SPT], pre_e[SPT];
 #pragma unroll
   for (int u = 0; u < SPT; ++u) {
@@ -319,10 +340,10 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
       pre_e[u] = a.topk_idx[slot0 + i];
     }
   }
-  const int pre_rt = tid < P ? a.ws_rank_tok[(size_t)tid * P + s] : 0;
+  const int pre_rt = tid < Pv ? a.ws_rank_tok[(size_t)tid * P + s] : 0;
   const int nsp = s < NS ? min(kSpecPerBlock, (NS - s + P - 1) / P) : 0;  // special ids of this workgroup
   int pre_sp = 0;
-  if (tid < P * nsp) pre_sp = a.ws_special[(size_t)(tid % P) * NS + s + (tid / P) * P];
+  if (tid < Pv * nsp) pre_sp = a.ws_special[(size_t)(tid % Pv) * NS + s + (tid / Pv) * P];
   if (tid == 0) acc_rt = 0;
   if (tid < kSpecPerBlock) acc_sp[tid] = 0;
 
@@ -330,17 +351,17 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
   for (int v = tid; v < E * G; v += 1024) {
     const int e = v % E, g = v / E;
     int tot = 0, below = 0;
-    column_sums(a.ws_cnt_t, E, e, P, g, G, s, tot, below);
+    column_sums(a.ws_cnt_t, E, e, Pv, g, G, s * m, tot, below);
     red_tot[v] = tot;
     red_pre[v] = below;
   }
   __syncthreads();
   if (pre_rt) atomicAdd(&acc_rt, pre_rt);
-  if (pre_sp) atomicAdd(&acc_sp[tid / P], pre_sp);
-  // columns longer than the workgroup (P > 1024) and further special ids (rare)
-  for (int i = tid + 1024; i < P; i += 1024) atomicAdd(&acc_rt, a.ws_rank_tok[(size_t)i * P + s]);
-  for (int e2 = tid + 1024; e2 < P * nsp; e2 += 1024)
-    atomicAdd(&acc_sp[e2 / P], a.ws_special[(size_t)(e2 % P) * NS + s + (e2 / P) * P]);
+  if (pre_sp) atomicAdd(&acc_sp[tid / Pv], pre_sp);
+  // columns longer than the workgroup (Pv > 1024) and further special ids (rare)
+  for (int i = tid + 1024; i < Pv; i += 1024) atomicAdd(&acc_rt, a.ws_rank_tok[(size_t)i * P + s]);
+  for (int e2 = tid + 1024; e2 < Pv * nsp; e2 += 1024)
+    atomicAdd(&acc_sp[e2 / Pv], a.ws_special[(size_t)(e2 % Pv) * NS + s + (e2 / Pv) * P]);
   for (int e = tid; e < E; e += 1024) {
     int tot = 0, below = 0;
     for (int g = 0; g < G; ++g) {
@@ -351,6 +372,24 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
     basel[e] = below;
   }
   __syncthreads();
+
+  // recv_counts column s, and the first row of each later sub-chunk relative to the chunk's
+  // (red is free since the barrier above)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = tid + 1024 * h;
+    if (SUBS && e < E) {
+      int run = sub[h][0];
+#pragma unroll
+      for (int qq = 1; qq < 4; ++qq) {
+        if (qq < m) {
+          subb[(qq - 1) * E + e] = run;
+          run += sub[h][qq];
+        }
+      }
+      a.recv_counts[(size_t)e * P + s] = run;
+    }
+  }
 
   // exclusive scan of totl[0..E): thread tid owns elements 2tid, 2tid+1
   const int e0 = 2 * tid, e1 = 2 * tid + 1;
@@ -385,9 +424,10 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
 
   // rows of this chunk's slots
   bool overflow = false;
-  auto finalize_slot = [&](int i, int v, int e) {  // v: the slot's rank in the chunk, or < 0
+  auto finalize_slot = [&](int i, int v, int e) {  // v: the slot's rank in its sub-chunk, or < 0
     if (v < 0) return;
-    const int row = basel[e] + v;
+    const int qq = SUBS ? (i / K) / a.BSv : 0;
+    const int row = basel[e] + (qq > 0 ? subb[(qq - 1) * E + e] : 0) + v;
     if (row >= liml[e]) {  // only a token repeating an expert id can overflow its window
       overflow = true;
       a.dst_row[slot0 + i] = -1;
@@ -408,7 +448,7 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
   // special ids beyond what P workgroups of kSpecPerBlock cover (NS > P kSpecPerBlock): summed here
   for (int z = s + kSpecPerBlock * P + tid * P; z < NS; z += 1024 * P) {
     int tot = 0, below = 0;
-    column_sums(a.ws_special, NS, z, P, 0, 1, 0, tot, below);
+    column_sums(a.ws_special, NS, z, Pv, 0, 1, 0, tot, below);
     a.special_counts[z] = tot;
   }
 
@@ -657,10 +697,13 @@ size_t layout_fused_lds_bytes(int waves, int E, int NS, int Epad, int Spad, int 
          (size_t)waves * Epad * 2 + (size_t)Spad * 2 + (rows ? (size_t)Spad * 4 : 0) + (size_t)BS;
 }
 
-// single launch while each workgroup's pass over every token stays small
+// single launch while each workgroup's pass over every token stays small, and its chunk too:
+// a chunk of more than 384 tokens is ranked faster by the two-launch path, which splits it
+// over several workgroups (measured: T=512, K=16, one rank 22.2 -> 17.4 us; T=1024, K=8, two
+// ranks 15.4 -> 13.2 us; at 384 tokens and below the single launch is as fast or faster)
 static bool use_fused(const LayoutArgs &a, bool rows) {
   const size_t flds = layout_fused_lds_bytes(layout_waves(a.E), a.E, a.NS, a.Epad, a.Spad, a.P, a.BS, rows);
-  return (int64_t)a.T * a.K <= kFusedMaxSlots && flds <= kMaxLds;
+  return (int64_t)a.T * a.K <= kFusedMaxSlots && a.BS <= kFusedMaxChunk && flds <= kMaxLds;
 }
 
 int layout_launch_count(const LayoutArgs &a) { return use_fused(a, false) ? 1 : 2; }
@@ -701,6 +744,25 @@ static hipError_t launch_fused_mode(const LayoutArgs &a, const DispatchArgs &d, 
   }
 }
 
+template <bool SUBS>
+static hipError_t launch_count(const LayoutArgs &b, int W, bool big, dim3 grid, size_t lds, hipStream_t stream) {
+  const void *fn = W == 16 ? (big ? (const void *)&layout_count_kernel<16, true, SUBS> : (const void *)&layout_count_kernel<16, false, SUBS>)
+                           : (big ? (const void *)&layout_count_kernel<8, true, SUBS> : (const void *)&layout_count_kernel<8, false, SUBS>);
+  if (lds > 65536) {  // gfx950 has 160 KB of LDS per workgroup; more than 64 KB must be asked for
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  if (W == 16 && big)
+    hipLaunchKernelGGL((layout_count_kernel<16, true, SUBS>), grid, dim3(16 * 64), lds, stream, b);
+  else if (W == 16)
+    hipLaunchKernelGGL((layout_count_kernel<16, false, SUBS>), grid, dim3(16 * 64), lds, stream, b);
+  else if (big)
+    hipLaunchKernelGGL((layout_count_kernel<8, true, SUBS>), grid, dim3(8 * 64), lds, stream, b);
+  else
+    hipLaunchKernelGGL((layout_count_kernel<8, false, SUBS>), grid, dim3(8 * 64), lds, stream, b);
+  return hipGetLastError();
+}
+
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {
   const int W = layout_waves(a.E);
   if (use_fused(a, false)) {
@@ -708,33 +770,26 @@ hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {
     return W == 16 ? launch_fused_mode<16>(a, none, -1, false, stream) : launch_fused_mode<8>(a, none, -1, false, stream);
   }
   const int S = a.BS * a.K;
-  // LDS match tables for chunks that give each wave several 64-slot groups, when they fit
+  // LDS match tables for sub-chunks that give each wave several 64-slot groups, when they fit
   LayoutArgs b = a;
-  const size_t base = layout_lds_bytes(W, a.Epad, a.Spad, a.P, a.NS, a.BS, 0);
+  const size_t base = layout_lds_bytes(W, a.Epad, a.Svpad, a.P, a.NS, a.BSv, 0);
   const int mw = a.E > a.P ? a.E : a.P;
-  const bool big = S > W * 64 && base + (size_t)W * mw * 8 <= kMaxLds;
+  const bool big = a.BSv * a.K > W * 64 && base + (size_t)W * mw * 8 <= kMaxLds;
   b.mt = big ? mw : 0;
-  const size_t lds = layout_lds_bytes(W, a.Epad, a.Spad, a.P, a.NS, a.BS, b.mt);
-  const void *fn = W == 16 ? (big ? (const void *)&layout_count_kernel<16, true> : (const void *)&layout_count_kernel<16, false>)
-                           : (big ? (const void *)&layout_count_kernel<8, true> : (const void *)&layout_count_kernel<8, false>);
-  if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  if (W == 16 && big)
-    hipLaunchKernelGGL((layout_count_kernel<16, true>), dim3(a.P), dim3(16 * 64), lds, stream, b);
-  else if (W == 16)
-    hipLaunchKernelGGL((layout_count_kernel<16, false>), dim3(a.P), dim3(16 * 64), lds, stream, b);
-  else if (big)
-    hipLaunchKernelGGL((layout_count_kernel<8, true>), dim3(a.P), dim3(8 * 64), lds, stream, b);
-  else
-    hipLaunchKernelGGL((layout_count_kernel<8, false>), dim3(a.P), dim3(8 * 64), lds, stream, b);
-  hipError_t err = hipGetLastError();
+  const size_t lds = layout_lds_bytes(W, a.Epad, a.Svpad, a.P, a.NS, a.BSv, b.mt);
+  const dim3 grid((unsigned)(a.P * a.m));
+  const bool subs = a.m > 1;
+  hipError_t err = subs ? launch_count<true>(b, W, big, grid, lds, stream) : launch_count<false>(b, W, big, grid, lds, stream);
   if (err != hipSuccess) return err;
-  if (S > 1024)  // every slot of the chunk loaded at the start
-    hipLaunchKernelGGL(layout_scan_finalize_kernel<8>, dim3(a.P), dim3(1024), 0, stream, a);
+  // with more than 1024 slots per chunk every slot is loaded at the start
+  if (S > 1024 && subs)
+    hipLaunchKernelGGL((layout_scan_finalize_kernel<8, true>), dim3(a.P), dim3(1024), 0, stream, a);
+  else if (S > 1024)
+    hipLaunchKernelGGL((layout_scan_finalize_kernel<8, false>), dim3(a.P), dim3(1024), 0, stream, a);
+  else if (subs)
+    hipLaunchKernelGGL((layout_scan_finalize_kernel<1, true>), dim3(a.P), dim3(1024), 0, stream, a);
   else
-    hipLaunchKernelGGL(layout_scan_finalize_kernel<1>, dim3(a.P), dim3(1024), 0, stream, a);
+    hipLaunchKernelGGL((layout_scan_finalize_kernel<1, false>), dim3(a.P), dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 

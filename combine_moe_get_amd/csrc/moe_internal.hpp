@@ -71,15 +71,16 @@ struct LayoutArgs {
   const int32_t *topk_idx;
   const uint8_t *mask;
   int32_t T, K, E, P, BS, L, NS, nbits, Epad, Spad;
+  int32_t m, BSv, Svpad;  // two-launch layout: sub-chunks per chunk, tokens per sub-chunk, padded slots
   int64_t Etot;
   int64_t rank_stride;  // 0: compact rows; A > 0: rank r owns rows [r A, r A + A)
   int32_t *cnt, *expert_offsets, *recv_counts, *special_counts, *num_tokens_per_rank,
       *rank_offsets, *dst_row, *src_info;
   uint8_t *itr;
   uint32_t *status;
-  int32_t *ws_cnt_t;     // [P][E]  routed copies of expert e sent by rank s
-  int32_t *ws_rank_tok;  // [P][P]  per source rank: tokens with a copy on rank r
-  int32_t *ws_special;   // [P][NS] per source rank: special slots per id
+  int32_t *ws_cnt_t;     // [P m][E]  routed copies of expert e sent by sub-chunk v
+  int32_t *ws_rank_tok;  // [P m][P]  per sub-chunk: tokens with a copy on rank r
+  int32_t *ws_special;   // [P m][NS] per sub-chunk: special slots per id
   int32_t mt;            // 64-bit words per wave of the count kernel's LDS match tables; set by the launcher
 };
 
@@ -105,6 +106,16 @@ struct CombineArgs {
   uint16_t *out;
   int32_t T, H, K, E, Z, C, Kc;
 };
+
+// Sub-chunks per source rank in the two-launch layout: a chunk of more than 128 tokens is
+// counted by up to 4 workgroups, as long as the count matrix keeps at most 64 rows (every
+// workgroup of the scan kernel sums all of them) and m E <= 4096 (the scan kernel's LDS).
+inline int layout_subchunks(int BS, int E, int P) {
+  int m = (BS + 127) / 128;
+  if (m > 4) m = 4;
+  while (m > 1 && (m * E > 4096 || m * P > 64)) --m;
+  return m < 1 ? 1 : m;
+}
 
 // ---- launchers (return hipSuccess or the launch error) ---------------------
 

@@ -113,13 +113,17 @@ def test_fused_named_workloads(cid, T, P, launches):
                 label=f"workload {cid} ({c['name']})", expect_launches=launches)
 
 
-@pytest.mark.parametrize("case", ["wide_E", "max_slots", "ragged_H", "max_H", "empty", "per_expert_share"])
+@pytest.mark.parametrize("case", ["wide_E", "max_slots", "big_chunk", "ragged_H", "max_H", "empty", "per_expert_share"])
 def test_fused_edge_cases(case):
     r = workloads.rng_for(11, 77, 0)
+    launches = 1
     if case == "wide_E":  # E > 1024: 8-wave workgroups
         T, H, K, E, P = 64, 1024, 16, 2048, 2
-    elif case == "max_slots":  # T * K = 8192 exactly, one rank with 512 tokens
+    elif case == "max_slots":  # T * K = 8192 exactly, two ranks of 256 tokens
+        T, H, K, E, P = 512, 2048, 16, 64, 2
+    elif case == "big_chunk":  # one rank of 512 tokens: two layout launches (split chunk) + dispatch
         T, H, K, E, P = 512, 2048, 16, 64, 1
+        launches = 3
     elif case == "ragged_H":
         T, H, K, E, P = 96, 520, 4, 32, 4
     elif case == "max_H":
@@ -134,7 +138,7 @@ def test_fused_edge_cases(case):
     smooth = r.uniform(0.5, 1.5, (E, H) if case in ("wide_E", "per_expert_share") else H).astype(np.float32)
     for qm in (0, 1, 2):
         n = check_fused(T, H, K, E, P, 0, 0, 0, topk, None, x, w, qm, smooth if qm else None, label=case)
-        assert n == 1
+        assert n == (launches if T else 1)
 
 
 @pytest.mark.parametrize("T", [128, 4096])  # the single kernel, and the layout kernels + dispatch
