@@ -392,6 +392,34 @@ def test_two_launch_layout_rank_and_special_totals(P, BS, K, E, Z, C, Kc):
     G.assert_layout_equal(G.layout_to_numpy(lay), lo)
 
 
+@pytest.mark.parametrize("P,BS,K,E,Z,stride", [(4, 129, 16, 64, 2, 0),   # 2 sub-chunks of 65 / 64 tokens
+                                                (2, 257, 16, 96, 0, -1),  # 3 of 86 / 86 / 85, rank windows
+                                                (1, 385, 8, 256, 3, 0),   # 4 of 97 / 97 / 97 / 94, one rank
+                                                (3, 511, 8, 48, 1, -1),   # 4 of 128 / 128 / 128 / 127
+                                                (8, 200, 6, 32, 2, 0)])   # 2 of 100, odd top-k
+def test_two_launch_layout_split_chunks(P, BS, K, E, Z, stride):
+    # chunks of more than 128 tokens are counted by several workgroups (ragged last sub-chunk);
+    # the scan kernel adds the earlier sub-chunks' counts
+    T = P * BS
+    r = np.random.default_rng(BS)
+    etot = E + Z
+    topk = r.integers(0, etot, size=(T, K)).astype(np.int32)
+    topk[r.random((T, K)) < 0.05] = -1
+    mask = (r.random(T) < 0.9).astype(np.uint8)
+    shape, osh = G.shapes(T, 64, K, E, P, Z)
+    assert mg.layout_launches(shape) == 2
+    A = mg.rank_capacity(shape) if stride else 0
+    print(f"[case] split chunks P={P} BS={BS} K={K} E={E} Z={Z} A={A}", flush=True)
+    lo = oracle.layout(osh, topk, mask, rank_stride=A)
+    lay = mg.layout(shape, G.dev(topk), G.dev(mask), rank_stride=A)
+    torch.cuda.synchronize()
+    g = G.layout_to_numpy(lay, A)
+    if A:
+        rows = np.sort(lo["dst_row"][lo["dst_row"] >= 0])
+        g["src_info"], lo["src_info"] = g["src_info"][rows], lo["src_info"][rows]
+    G.assert_layout_equal(g, lo)
+
+
 @pytest.mark.parametrize("qm", [1, 2])
 def test_per_expert_smooth_scales_full_size(qm):
     # the decode workload with [E, H] smooth scales (each copy quantized with its expert's row)
