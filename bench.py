@@ -505,6 +505,21 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False)
     k_lay = kernel_avg_ms(lambda g: g["c_lay"](stream))
     status = max(int(g["lay"].status[0]) for g in gsets)
 
+    # the same dispatch kernel writing the same copies in token-major order (row = index of the
+    # copy in (token, slot) order): what the expert-major placement the layout prescribes costs
+    row_probe = None
+    if args.row_probe:
+        for g in gsets:
+            valid = g["lay"].dst_row >= 0
+            tm = torch.cumsum(valid.flatten().to(torch.int32), 0, dtype=torch.int32).view_as(valid) - 1
+            g["tm_rows"] = torch.where(valid, tm, torch.full_like(tm, -1)).contiguous()
+            g["c_dis_tm"] = mg.prepare_dispatch(shape, qm, g["x"], g["tm_rows"], g["smooth"], None, g["topk"],
+                                                g["ex"], g["ds"], rows=cap)
+        k_tm = kernel_avg_ms(lambda g: g["c_dis_tm"](stream))
+        row_probe = dict(expert_major_us=round(k_dis * 1e3, 2), token_major_us=round(k_tm * 1e3, 2),
+                         what="dispatch kernel, same copies and bytes, rows in expert-major (the layout's) "
+                              "or token-major order")
+
     # the step with layout + dispatch through moe_layout_dispatch (one kernel for T * K <= 8192)
     fused = None
     if graphs is None:
@@ -597,6 +612,8 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False)
     }
     if fused is not None:
         line["fused_layout_dispatch"] = fused
+    if row_probe is not None:
+        line["row_placement_probe"] = row_probe
     return line, sets[0]
 
 
@@ -633,6 +650,8 @@ def main():
                     help="skip the HBM probe (fill and copy of a 2 GiB buffer with library kernels)")
     ap.add_argument("--no-share", action="store_true",
                     help="skip the extra measurement of one rank's share (T = BS, P = 1)")
+    ap.add_argument("--row-probe", action="store_true",
+                    help="also time the dispatch kernel with token-major receive rows (write-pattern probe)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run a plain 512 MiB device copy 3x (counter calibration)")
     args = ap.parse_args()
