@@ -39,7 +39,6 @@ int layout_waves(int E) { return E <= 1024 ? 16 : 8; }
 // the single-launch layout re-reads every token's ids in each of the P workgroups; that pass is
 // latency-bound, so it only pays while it is short (one launch saved)
 static constexpr int64_t kFusedMaxSlots = 8192;  // measured: faster below ~10K slots, slower above
-static constexpr int kFusedMaxChunk = 384;         // tokens per source rank (see use_fused)
 static constexpr size_t kMaxLds = 160 * 1024;  // gfx950 LDS per workgroup
 static constexpr int kSpecPerBlock = 8;        // special-id totals one scan workgroup sums from its prefetch
 
@@ -463,47 +462,56 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
 
 
 // ---- single-launch layout ---------------------------------------------------
-// One workgroup per source rank s, no communication between workgroups: each
-// first histograms the ids of ALL tokens (slot-parallel, LDS integer atomics --
-// counts do not depend on order), split into tokens of ranks below s (hist_lo)
-// and the rest (hist_hi).  Expert totals are hist_lo + hist_hi, the first row of
-// (s, e) is offset[e] + hist_lo[e]; the chunk's own slots are then ranked in order
-// with the ballot match and written as final rows.  Workgroup 0 also writes the
+// Workgroup (s, m) owns tokens [m tpw, m tpw + nt) of source rank s's chunk (a
+// sub-chunk), with no communication between workgroups: each first histograms
+// the ids of ALL tokens (slot-parallel, LDS integer atomics -- counts do not
+// depend on order) into three bins: tokens before its sub-chunk (hist_lo), the
+// rest of chunk s from the sub-chunk on (hist_mid) and the tokens after chunk s
+// (hist_hi).  Expert totals are lo + mid + hi and the first row of the sub-chunk
+// in expert e is offset[e] + hist_lo[e]; the sub-chunk's own slots are then ranked
+// in order with the ballot match and written as final rows.  Workgroup (s, 0)
+// also writes recv_counts[:, s] (its hist_mid is chunk s), workgroup (0, 0) the
 // per-expert / per-rank outputs (it saw every token).  Used while the redundant
 // pass stays small (T * K bounded); larger worlds take the two-launch path.
 //
 // With DM >= 0 the same kernel also dispatches (layout + dispatch in one launch,
-// as the CANN dispatch op returns both): the grid is P x M workgroups, workgroup
-// (s, m) computes chunk s's layout like the others (only m == 0 writes it) and
-// then quantizes / copies tokens [m tpw, m tpw + tpw) of the chunk with the rows
-// it holds in LDS (dispatch_token_block; DM = quant mode, PE = per-expert scales).
-template <int W, int DM, bool PE>
+// as the CANN dispatch op returns both): each workgroup quantizes / copies its own
+// tokens with the rows it holds in LDS (dispatch_token_block; DM = quant mode, PE =
+// per-expert scales).
+// SUB: the chunk is split (M > 1 workgroups per chunk); otherwise two bins suffice (hist_hi
+// then holds chunk s too) and recv_counts comes from the chunk's own ranking.
+template <int W, int DM, bool PE, bool SUB>
 __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, DispatchArgs d, int tpw) {
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ int wsum[16];
   __shared__ float red[2][16];
   constexpr int NT = W * 64;
   const int s = blockIdx.x;
-  const bool writer = blockIdx.y == 0;  // writes the layout outputs of chunk s
+  const bool writer = blockIdx.y == 0;  // writes recv_counts[:, s]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int T = a.T, K = a.K, E = a.E, P = a.P, BS = a.BS, NS = a.NS;
   const int Etot = E + NS;
   const int Ep2 = (Etot + 1) & ~1;
-  const int S = BS * K;
-  const int t0 = s * BS;
-  const size_t slot0 = (size_t)t0 * K;
+  const int tq = (int)blockIdx.y * tpw;          // first token of the sub-chunk inside the chunk
+  const int nt = max(0, min(BS, tq + tpw) - tq);  // its tokens
+  const int S = nt * K;
+  const int Sp = tpw * K + ((tpw * K) & 1);
+  const int cend = (s + 1) * BS;                 // end of chunk s
+  const int u0 = s * BS + tq;                    // first token of the sub-chunk
+  const size_t slot0 = (size_t)u0 * K;
 
-  int *hist_lo = (int *)lds;                     // [Ep2] ids of tokens of ranks < s
-  int *hist_hi = hist_lo + Ep2;                  // [Ep2] ids of tokens of ranks >= s
+  int *hist_lo = (int *)lds;                     // [Ep2] ids of tokens before the sub-chunk
+  int *hist_mid = hist_lo + Ep2;                 // [Ep2] ids of the sub-chunk and the rest of chunk s
+  int *hist_hi = hist_mid + Ep2;                 // [Ep2] ids of tokens after chunk s
   int *rtok = hist_hi + Ep2;                     // [P]  distinct tokens per rank (block 0)
   int *offl = rtok + P;                          // [E + 1]
   int *basel = offl + E + 1;                     // [E]
   int *liml = basel + E;                         // [E]
-  int *ids = liml + E;                           // [Spad]
-  uint16_t *cnt = (uint16_t *)(ids + a.Spad);    // [W][Epad]
-  uint16_t *rk = cnt + W * a.Epad;               // [Spad]
-  int *rows = (int *)(rk + a.Spad);              // [Spad] final rows (DM >= 0 only)
-  uint8_t *act = DM >= 0 ? (uint8_t *)(rows + a.Spad) : (uint8_t *)(rk + a.Spad);  // [BS]
+  int *ids = liml + E;                           // [Sp]
+  uint16_t *cnt = (uint16_t *)(ids + Sp);        // [W][Epad]
+  uint16_t *rk = cnt + W * a.Epad;               // [Sp]
+  int *rows = (int *)(rk + Sp);                  // [Sp] final rows (DM >= 0 only)
+  uint8_t *act = DM >= 0 ? (uint8_t *)(rows + Sp) : (uint8_t *)(rk + Sp);  // [tpw]
 
   // loads issued before the first barrier, so their latency overlaps the set-up below:
   // this lane's slot of the first pass over all tokens, and the first token this
@@ -519,22 +527,21 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
     }
   }
   TokenPrefetch pf;
-  const int tl_first = (int)blockIdx.y * tpw;
   if constexpr (DM >= 0) {
-    if (tl_first < BS) dispatch_prefetch<DM, PE>(d, t0 + tl_first, pf);
+    if (nt > 0) dispatch_prefetch<DM, PE>(d, u0, pf);
   }
 
-  for (int i = tid; i < 2 * Ep2; i += NT) hist_lo[i] = 0;
+  for (int i = tid; i < 3 * Ep2; i += NT) hist_lo[i] = 0;  // (hist_mid stays 0 without SUB)
   for (int i = tid; i < P; i += NT) rtok[i] = 0;
   for (int i = tid; i < W * a.Epad / 2; i += NT) ((uint32_t *)cnt)[i] = 0u;
   for (int i = tid; i < S; i += NT) ids[i] = a.topk_idx[slot0 + i];
-  for (int i = tid; i < BS; i += NT) act[i] = a.mask ? a.mask[t0 + i] : (uint8_t)1;
-  if (writer) zero_bytes(a.itr + (size_t)t0 * P, (size_t)BS * P, tid, NT);
+  for (int i = tid; i < nt; i += NT) act[i] = a.mask ? a.mask[u0 + i] : (uint8_t)1;
+  zero_bytes(a.itr + (size_t)u0 * P, (size_t)nt * P, tid, NT);
   __syncthreads();
   const bool first = writer && s == 0;  // the workgroup that writes the per-expert / per-rank outputs
 
-  // ---- every token's ids (slot-parallel): totals, counts below this rank, distinct
-  //      tokens per rank (first workgroup) ------------------------------------------
+  // ---- every token's ids (slot-parallel): totals, counts before the sub-chunk, chunk s's
+  //      counts, distinct tokens per rank (first workgroup) --------------------------------
   bool bad = false;
   {
     const int nbp = 32 - __builtin_clz((unsigned)P);
@@ -556,7 +563,7 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
         if (id < 0 || id >= Etot) {
           bad = true;
         } else {
-          atomicAdd(&(t < t0 ? hist_lo : hist_hi)[id], 1);
+          atomicAdd(&(t < u0 ? hist_lo : (SUB && t < cend) ? hist_mid : hist_hi)[id], 1);
           if (id < E) own = id / a.L;
         }
       }
@@ -566,15 +573,13 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
     }
   }
 
-  // ---- this chunk: is_token_in_rank rows ------------------------------------------
-  if (writer) {
-    for (int i = tid; i < S; i += NT) {
-      const int id = ids[i];
-      if (id >= 0 && id < E && act[i / K]) a.itr[(size_t)t0 * P + (size_t)(i / K) * P + id / a.L] = 1;
-    }
+  // ---- this sub-chunk: is_token_in_rank rows --------------------------------------
+  for (int i = tid; i < S; i += NT) {
+    const int id = ids[i];
+    if (id >= 0 && id < E && act[i / K]) a.itr[(size_t)u0 * P + (size_t)(i / K) * P + id / a.L] = 1;
   }
 
-  // ---- this chunk: stable ranks inside each wave segment (ballot match) -------
+  // ---- this sub-chunk: stable ranks inside each wave segment (ballot match) -------
   const int seg = (((S + W - 1) / W) + 63) & ~63;
   const int beg = wv * seg;
   const int end = min(S, beg + seg);
@@ -586,12 +591,7 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
       const int id = ids[i];
       if (act[i / K] && id >= 0 && id < E) key = id;
     }
-    uint64_t peers = ~0ull;
-    for (int b = 0; b < a.nbits; ++b) {
-      const bool bit = (key >> b) & 1;
-      const uint64_t bl = ballot(bit);
-      peers &= bit ? bl : ~bl;
-    }
+    const uint64_t peers = match_key(key, a.nbits);
     if (key < E) {
       const int r = (int)mycnt[key] + popc_below(peers);
       rk[i] = (uint16_t)r;
@@ -600,10 +600,10 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
   }
   __syncthreads();
 
-  // ---- per expert: scan over the waves (chunk-local bases), recv_counts column ---
+  // ---- per expert: scan over the waves (sub-chunk-local bases); recv_counts column ---
   for (int e = tid; e < E; e += NT) {
     const int run = scan_wave_counts<W>(cnt, a.Epad, e);
-    if (writer) a.recv_counts[(size_t)e * P + s] = run;
+    if (writer) a.recv_counts[(size_t)e * P + s] = SUB ? hist_mid[e] : run;
   }
 
   // ---- expert offsets: exclusive scan of the totals (each thread 2 * ceil(E / 2NT) experts) ---
@@ -613,7 +613,7 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int e = tid * PER + u;
-      v[u] = e < E ? hist_lo[e] + hist_hi[e] : 0;
+      v[u] = e < E ? hist_lo[e] + (SUB ? hist_mid[e] : 0) + hist_hi[e] : 0;
       local += v[u];
     }
     const int incl = wave_inclusive_sum(local);
@@ -647,7 +647,7 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
   }
   __syncthreads();
 
-  // ---- rows of this chunk ---------------------------------------------------------
+  // ---- rows of this sub-chunk -----------------------------------------------------
   bool overflow = false;
   for (int base = beg; base < end; base += 64) {
     const int i = base + lane;
@@ -659,14 +659,14 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
       if (row >= liml[id]) {  // only a token repeating an expert id can overflow its window
         overflow = true;
         row = -1;
-      } else if (writer) {
+      } else {
         a.src_info[row] = (int)(slot0 + i);
       }
     }
-    if (writer) a.dst_row[slot0 + i] = row;
+    a.dst_row[slot0 + i] = row;
     if constexpr (DM >= 0) rows[i] = row;
   }
-  if (writer && overflow) atomicOr(a.status, (uint32_t)MOE_DEV_STATUS_RANK_OVERFLOW);
+  if (overflow) atomicOr(a.status, (uint32_t)MOE_DEV_STATUS_RANK_OVERFLOW);
 
   if (first) {
     if (bad) atomicOr(a.status, (uint32_t)MOE_DEV_STATUS_BAD_EXPERT_ID);
@@ -677,33 +677,39 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
     if (tid == 0) a.expert_offsets[E] = offl[E];
     for (int r = tid; r <= P; r += NT) a.rank_offsets[r] = offl[r * a.L];
     for (int r = tid; r < P; r += NT) a.num_tokens_per_rank[r] = rtok[r];
-    for (int z = tid; z < NS; z += NT) a.special_counts[z] = hist_lo[E + z] + hist_hi[E + z];
+    for (int z = tid; z < NS; z += NT) a.special_counts[z] = hist_lo[E + z] + (SUB ? hist_mid[E + z] : 0) + hist_hi[E + z];
   }
 
   if constexpr (DM >= 0) {
-    // ---- dispatch of this workgroup's tokens of the chunk -------------------------
+    // ---- dispatch of this workgroup's tokens ----------------------------------------
     __syncthreads();  // rows[] complete
     int par = 0;
-    const int tl0 = (int)blockIdx.y * tpw;
-    const int tl1 = min(BS, tl0 + tpw);
-    for (int tl = tl0; tl < tl1; ++tl)
-      dispatch_token_block<DM, PE>(d, t0 + tl, rows + tl * K, ids + tl * K, red, par, pf, tl == tl_first);
+    for (int tl = 0; tl < nt; ++tl)
+      dispatch_token_block<DM, PE>(d, u0 + tl, rows + tl * K, ids + tl * K, red, par, pf, tl == 0);
   }
 }
 
-size_t layout_fused_lds_bytes(int waves, int E, int NS, int Epad, int Spad, int P, int BS, bool rows) {
+// dynamic LDS of layout_fused_kernel for sub-chunks of tpw tokens
+size_t layout_fused_lds_bytes(int waves, int E, int NS, int Epad, int K, int P, int tpw, bool rows) {
   const size_t ep2 = (size_t)((E + NS + 1) & ~1);
-  return 2 * ep2 * 4 + (size_t)P * 4 + (size_t)(E + 1) * 4 + 2 * (size_t)E * 4 + (size_t)Spad * 4 +
-         (size_t)waves * Epad * 2 + (size_t)Spad * 2 + (rows ? (size_t)Spad * 4 : 0) + (size_t)BS;
+  const size_t sp = (size_t)tpw * K + (((size_t)tpw * K) & 1);
+  return 3 * ep2 * 4 + (size_t)P * 4 + (size_t)(E + 1) * 4 + 2 * (size_t)E * 4 + sp * 4 +
+         (size_t)waves * Epad * 2 + sp * 2 + (rows ? sp * 4 : 0) + (size_t)tpw;
 }
 
-// single launch while each workgroup's pass over every token stays small, and its chunk too:
-// a chunk of more than 384 tokens is ranked faster by the two-launch path, which splits it
-// over several workgroups (measured: T=512, K=16, one rank 22.2 -> 17.4 us; T=1024, K=8, two
-// ranks 15.4 -> 13.2 us; at 384 tokens and below the single launch is as fast or faster)
+// tokens per workgroup of the single-launch kernel: layout only, sub-chunks of at most 32
+// tokens (more workgroups share the ranking); with the dispatch, about 256 workgroups over the
+// world, at least one token each
+static int fused_tpw(const LayoutArgs &a, bool dispatch) {
+  int tpw = dispatch ? (a.T + 255) / 256 : (a.BS < 32 ? a.BS : 32);
+  if (tpw > a.BS) tpw = a.BS;
+  return tpw < 1 ? 1 : tpw;
+}
+
+// single launch while each workgroup's pass over every token stays small
 static bool use_fused(const LayoutArgs &a, bool rows) {
-  const size_t flds = layout_fused_lds_bytes(layout_waves(a.E), a.E, a.NS, a.Epad, a.Spad, a.P, a.BS, rows);
-  return (int64_t)a.T * a.K <= kFusedMaxSlots && a.BS <= kFusedMaxChunk && flds <= kMaxLds;
+  const size_t flds = layout_fused_lds_bytes(layout_waves(a.E), a.E, a.NS, a.Epad, a.K, a.P, fused_tpw(a, rows), rows);
+  return (int64_t)a.T * a.K <= kFusedMaxSlots && flds <= kMaxLds;
 }
 
 int layout_launch_count(const LayoutArgs &a) { return use_fused(a, false) ? 1 : 2; }
@@ -715,22 +721,23 @@ int layout_dispatch_launch_count(const LayoutArgs &a) {
 
 template <int W, int DM, bool PE>
 static hipError_t launch_fused(const LayoutArgs &a, const DispatchArgs &d, hipStream_t stream) {
-  const size_t flds = layout_fused_lds_bytes(W, a.E, a.NS, a.Epad, a.Spad, a.P, a.BS, DM >= 0);
+  const int tpw = fused_tpw(a, DM >= 0);
+  const size_t flds = layout_fused_lds_bytes(W, a.E, a.NS, a.Epad, a.K, a.P, tpw, DM >= 0);
+  int M = (a.BS + tpw - 1) / tpw;  // sub-chunks per chunk
+  if (M < 1) M = 1;
   // gfx950 has 160 KB of LDS per workgroup; more than 64 KB must be asked for
   if (flds > 65536) {
-    const hipError_t e = hipFuncSetAttribute((const void *)&layout_fused_kernel<W, DM, PE>,
+    const hipError_t e = hipFuncSetAttribute(M > 1 ? (const void *)&layout_fused_kernel<W, DM, PE, true>
+                                                   : (const void *)&layout_fused_kernel<W, DM, PE, false>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)flds);
     if (e != hipSuccess) return e;
   }
-  int tpw = 1, M = 1;
-  if (DM >= 0) {  // about 256 workgroups over the world, at least one token each
-    tpw = (a.T + 255) / 256;
-    if (tpw < 1) tpw = 1;
-    M = (a.BS + tpw - 1) / tpw;
-    if (M < 1) M = 1;
-  }
-  hipLaunchKernelGGL((layout_fused_kernel<W, DM, PE>), dim3((unsigned)a.P, (unsigned)M), dim3(W * 64), flds, stream,
-                     a, d, tpw);
+  if (M > 1)
+    hipLaunchKernelGGL((layout_fused_kernel<W, DM, PE, true>), dim3((unsigned)a.P, (unsigned)M), dim3(W * 64), flds,
+                       stream, a, d, tpw);
+  else
+    hipLaunchKernelGGL((layout_fused_kernel<W, DM, PE, false>), dim3((unsigned)a.P, 1u), dim3(W * 64), flds, stream,
+                       a, d, tpw);
   return hipGetLastError();
 }
 

@@ -101,9 +101,8 @@ int64_t moe_get_recv_capacity(const moe_get_shape_t *shape);
 int64_t moe_get_rank_capacity(const moe_get_shape_t *shape);
 
 /* Kernel launches one moe_get_layout / moe_get_layout_ex call makes for this
- * shape: 1 (T * K <= 8192 slots and at most 384 tokens per rank: every
- * workgroup histograms all ids itself) or 2 (a count kernel, then a
- * scan-and-finalize kernel).  For profiling and
+ * shape: 1 (T * K <= 8192 slots: every workgroup histograms all ids itself)
+ * or 2 (a count kernel, then a scan-and-finalize kernel).  For profiling and
  * launch accounting only; a negative MOE_ERR_* for an invalid shape. */
 int moe_get_layout_launches(const moe_get_shape_t *shape);
 
@@ -188,7 +187,7 @@ int moe_dispatch(const moe_get_shape_t *shape, int32_t quant_mode, const uint16_
  * identical, bit for bit, to moe_get_layout_ex(shape, rank_stride, ...)
  * followed by moe_dispatch(shape, quant_mode, ...) with the same arguments;
  * argument rules and errors are the union of theirs.  Small worlds (T * K <=
- * 8192 slots, at most 384 tokens per rank) run as a single kernel -- every workgroup derives its chunk's
+ * 8192 slots) run as a single kernel -- every workgroup derives its chunk's
  * rows itself and dispatches a share of the chunk's tokens -- which saves the
  * launches between layout and dispatch on the decode-sized batches the
  * low-latency kernels target; larger worlds run the layout kernels, then the

@@ -118,6 +118,7 @@ def test_layout_launches():
     assert mg.layout_launches(mg.make_shape(1056, 7168, 8, 256, 32)) == 2
     assert mg.layout_launches(mg.make_shape(4096, 7168, 8, 256, 32)) == 2
     assert mg.layout_launches(mg.make_shape(512, 7168, 16, 256, 2)) == 1  # 8192 slots, 256 tokens per rank
-    assert mg.layout_launches(mg.make_shape(512, 7168, 16, 256, 1)) == 2  # a 512-token chunk is split
+    assert mg.layout_launches(mg.make_shape(512, 7168, 16, 256, 1)) == 1  # one 512-token rank, 8192 slots
+    assert mg.layout_launches(mg.make_shape(1024, 7168, 16, 256, 2)) == 2  # 16384 slots
     with pytest.raises(mg.MoeGetError):
         mg.layout_launches(mg.make_shape(100, 7168, 8, 256, 32))  # T not a multiple of P

@@ -113,7 +113,8 @@ def test_fused_named_workloads(cid, T, P, launches):
                 label=f"workload {cid} ({c['name']})", expect_launches=launches)
 
 
-@pytest.mark.parametrize("case", ["wide_E", "max_slots", "big_chunk", "ragged_H", "max_H", "empty", "per_expert_share"])
+@pytest.mark.parametrize("case", ["wide_E", "max_slots", "big_chunk", "ragged_chunks", "big_world", "ragged_H",
+                                  "max_H", "empty", "per_expert_share"])
 def test_fused_edge_cases(case):
     r = workloads.rng_for(11, 77, 0)
     launches = 1
@@ -121,8 +122,12 @@ def test_fused_edge_cases(case):
         T, H, K, E, P = 64, 1024, 16, 2048, 2
     elif case == "max_slots":  # T * K = 8192 exactly, two ranks of 256 tokens
         T, H, K, E, P = 512, 2048, 16, 64, 2
-    elif case == "big_chunk":  # one rank of 512 tokens: two layout launches (split chunk) + dispatch
+    elif case == "big_chunk":  # one rank of 512 tokens in one launch (workgroups of 2 tokens each)
         T, H, K, E, P = 512, 2048, 16, 64, 1
+    elif case == "ragged_chunks":  # 100 tokens per rank: single-launch workgroups of 32, 32, 32, 4 tokens
+        T, H, K, E, P = 200, 512, 6, 40, 2
+    elif case == "big_world":  # T * K above the single-launch bound: two layout launches + dispatch
+        T, H, K, E, P = 1024, 1024, 16, 64, 2
         launches = 3
     elif case == "ragged_H":
         T, H, K, E, P = 96, 520, 4, 32, 4

@@ -394,7 +394,7 @@ def test_two_launch_layout_rank_and_special_totals(P, BS, K, E, Z, C, Kc):
 
 @pytest.mark.parametrize("P,BS,K,E,Z,stride", [(4, 129, 16, 64, 2, 0),   # 2 sub-chunks of 65 / 64 tokens
                                                 (2, 257, 16, 96, 0, -1),  # 3 of 86 / 86 / 85, rank windows
-                                                (1, 385, 8, 256, 3, 0),   # 4 of 97 / 97 / 97 / 94, one rank
+                                                (3, 385, 8, 255, 3, 0),   # 4 of 97 / 97 / 97 / 94
                                                 (3, 511, 8, 48, 1, -1),   # 4 of 128 / 128 / 128 / 127
                                                 (8, 200, 6, 32, 2, 0)])   # 2 of 100, odd top-k
 def test_two_launch_layout_split_chunks(P, BS, K, E, Z, stride):
