@@ -168,27 +168,31 @@ __global__ void __launch_bounds__(W * 64) layout_count_kernel(LayoutArgs a) {
   uint16_t *rk = cnt + W * a.Epad;              // [Svpad] rank of a slot inside its wave segment
   int *rank_tok = (int *)(rk + a.Svpad);        // [P]
   int *spec = rank_tok + P;                     // [NS]
-  uint8_t *act = (uint8_t *)(spec + NS);        // [BSv] token active flags
 
-  // one coalesced pass over the chunk's ids and mask; everything after reads LDS
+  // one coalesced pass over the chunk's ids and mask; everything after reads LDS.  A slot of
+  // an inactive token is stored as -1 (dropped), so no later pass looks at the mask.
   if constexpr (BIG) {  // every load issued before the first LDS store (S <= 512 * 16)
     constexpr int PER = 8192 / (W * 64);
     int v[PER];
+    uint8_t on[PER];
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int i = tid + u * W * 64;
       v[u] = i < S ? a.topk_idx[slot0 + i] : 0;
+      on[u] = (i < S && a.mask) ? a.mask[t0 + i / K] : (uint8_t)1;
     }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int i = tid + u * W * 64;
-      if (i < S) ids[i] = v[u];
+      if (i < S) ids[i] = on[u] ? v[u] : -1;
     }
     for (int i = tid; i < W * mt; i += W * 64) ((uint64_t *)lds)[i] = 0ull;
   } else {
-    for (int i = tid; i < S; i += W * 64) ids[i] = a.topk_idx[slot0 + i];
+    for (int i = tid; i < S; i += W * 64) {
+      const int v = a.topk_idx[slot0 + i];
+      ids[i] = (!a.mask || a.mask[t0 + i / K]) ? v : -1;
+    }
   }
-  for (int i = tid; i < nt; i += W * 64) act[i] = a.mask ? a.mask[t0 + i] : (uint8_t)1;
   for (int i = tid; i < W * a.Epad / 2; i += W * 64) ((uint32_t *)cnt)[i] = 0u;
   for (int i = tid; i < P; i += W * 64) rank_tok[i] = 0;
   for (int i = tid; i < NS; i += W * 64) spec[i] = 0;
@@ -203,7 +207,7 @@ __global__ void __launch_bounds__(W * 64) layout_count_kernel(LayoutArgs a) {
     for (int tb = wv * sl.per; tb < nt; tb += W * sl.per) {  // uniform per wave
       const int tl = tb + sl.g;
       int own = -1;
-      if (sl.on && tl < nt && act[tl]) {
+      if (sl.on && tl < nt) {
         const int id = ids[tl * K + sl.j];
         if (id == -1) {
         } else if (id < 0 || (int64_t)id >= a.Etot) {
@@ -231,7 +235,7 @@ __global__ void __launch_bounds__(W * 64) layout_count_kernel(LayoutArgs a) {
     int key = E;  // sentinel: not a routed slot
     if (i < end) {
       const int id = ids[i];
-      if (act[i / K] && id >= 0 && id < E) key = id;
+      if (id >= 0 && id < E) key = id;
     }
     // lanes holding the same key
     const uint64_t peers = BIG ? match_key_lds(mtab, key, key < E, lane) : match_key(key, a.nbits);
@@ -257,7 +261,7 @@ __global__ void __launch_bounds__(W * 64) layout_count_kernel(LayoutArgs a) {
     if (i < end) {
       const int id = ids[i];
       int r = -1;
-      if (act[i / K] && id >= 0 && id < E) r = (int)mycnt[id] + (int)rk[i];
+      if (id >= 0 && id < E) r = (int)mycnt[id] + (int)rk[i];
       a.dst_row[slot0 + i] = r;
     }
   }
@@ -511,7 +515,6 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
   uint16_t *cnt = (uint16_t *)(ids + Sp);        // [W][Epad]
   uint16_t *rk = cnt + W * a.Epad;               // [Sp]
   int *rows = (int *)(rk + Sp);                  // [Sp] final rows (DM >= 0 only)
-  uint8_t *act = DM >= 0 ? (uint8_t *)(rows + Sp) : (uint8_t *)(rk + Sp);  // [tpw]
 
   // loads issued before the first barrier, so their latency overlaps the set-up below:
   // this lane's slot of the first pass over all tokens, and the first token this
@@ -534,8 +537,10 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
   for (int i = tid; i < 3 * Ep2; i += NT) hist_lo[i] = 0;  // (hist_mid stays 0 without SUB)
   for (int i = tid; i < P; i += NT) rtok[i] = 0;
   for (int i = tid; i < W * a.Epad / 2; i += NT) ((uint32_t *)cnt)[i] = 0u;
-  for (int i = tid; i < S; i += NT) ids[i] = a.topk_idx[slot0 + i];
-  for (int i = tid; i < nt; i += NT) act[i] = a.mask ? a.mask[u0 + i] : (uint8_t)1;
+  for (int i = tid; i < S; i += NT) {  // a slot of an inactive token is stored as -1 (dropped)
+    const int v = a.topk_idx[slot0 + i];
+    ids[i] = (!a.mask || a.mask[u0 + i / K]) ? v : -1;
+  }
   zero_bytes(a.itr + (size_t)u0 * P, (size_t)nt * P, tid, NT);
   __syncthreads();
   const bool first = writer && s == 0;  // the workgroup that writes the per-expert / per-rank outputs
@@ -576,7 +581,7 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
   // ---- this sub-chunk: is_token_in_rank rows --------------------------------------
   for (int i = tid; i < S; i += NT) {
     const int id = ids[i];
-    if (id >= 0 && id < E && act[i / K]) a.itr[(size_t)u0 * P + (size_t)(i / K) * P + id / a.L] = 1;
+    if (id >= 0 && id < E) a.itr[(size_t)u0 * P + (size_t)(i / K) * P + id / a.L] = 1;
   }
 
   // ---- this sub-chunk: stable ranks inside each wave segment (ballot match) -------
@@ -589,7 +594,7 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
     int key = E;
     if (i < end) {
       const int id = ids[i];
-      if (act[i / K] && id >= 0 && id < E) key = id;
+      if (id >= 0 && id < E) key = id;
     }
     const uint64_t peers = match_key(key, a.nbits);
     if (key < E) {
@@ -654,7 +659,7 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
     if (i >= end) continue;
     const int id = ids[i];
     int row = -1;
-    if (act[i / K] && id >= 0 && id < E) {
+    if (id >= 0 && id < E) {
       row = basel[id] + (int)mycnt[id] + (int)rk[i];
       if (row >= liml[id]) {  // only a token repeating an expert id can overflow its window
         overflow = true;
