@@ -136,11 +136,11 @@ __device__ __forceinline__ int scan_wave_counts(uint16_t *cnt, int Epad, int e) 
   return run;
 }
 
-// BIG (chunks of more than W * 64 slots, so every wave ranks several 64-slot groups): the
-// id loads are all issued before the first LDS store, and slots are matched through LDS
-// tables (a.mt words per wave) instead of ballots.  Measured on gfx950: at 4096 slots per
-// chunk (T=8192, 16 ranks) the count kernel takes 9.6 instead of 10.8 us; at 1024 slots the
-// ballot version is faster.
+// BIG (sub-chunks of more than W * 64 slots, so every wave ranks several 64-slot groups):
+// the id loads are all issued before the first LDS store, and slots are matched through LDS
+// tables (a.mt words per wave) instead of ballots.  Measured on gfx950 (whole layout, chunks
+// not yet split): 4096 slots per chunk 18.4 -> 16.3 us, 2048 slots 16.3 -> 15.7 us; at 1024
+// slots the ballot version is as fast or faster.
 //
 // Workgroup v counts sub-chunk v = s m + q: tokens [q BSv, q BSv + nt) of source rank s's
 // chunk (m = 1 and BSv = BS unless chunks of more than 128 tokens are split, so that more
