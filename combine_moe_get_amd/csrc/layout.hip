@@ -149,8 +149,8 @@ __device__ __forceinline__ int scan_wave_counts(uint16_t *cnt, int Epad, int e) 
 template <int W, bool BIG, bool SUBS>
 __global__ void __launch_bounds__(W * 64) layout_count_kernel(LayoutArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
-  const int v = blockIdx.x;
-  const int s = SUBS ? v / a.m : v, q = v - s * a.m;
+  const int vs = blockIdx.x;  // sub-chunk index s m + q
+  const int s = SUBS ? vs / a.m : vs, q = vs - s * a.m;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
@@ -225,7 +225,7 @@ __global__ void __launch_bounds__(W * 64) layout_count_kernel(LayoutArgs a) {
     }
   }
 
-  // ---- ranking phase: wave wv owns slots [beg, end) of the chunk ------------
+  // ---- ranking phase: wave wv owns slots [beg, end) of the sub-chunk --------
   const int seg = (((S + W - 1) / W) + 63) & ~63;
   const int beg = wv * seg;
   const int end = min(S, beg + seg);
@@ -251,7 +251,7 @@ __global__ void __launch_bounds__(W * 64) layout_count_kernel(LayoutArgs a) {
   for (int e = tid; e < E; e += W * 64) {
     const int run = scan_wave_counts<W>(cnt, a.Epad, e);
     if constexpr (!SUBS) a.recv_counts[(size_t)e * P + s] = run;  // split chunks: the scan kernel sums
-    a.ws_cnt_t[(size_t)v * E + e] = run;
+    a.ws_cnt_t[(size_t)vs * E + e] = run;
   }
   __syncthreads();
 
@@ -265,8 +265,8 @@ __global__ void __launch_bounds__(W * 64) layout_count_kernel(LayoutArgs a) {
       a.dst_row[slot0 + i] = r;
     }
   }
-  for (int r = tid; r < P; r += W * 64) a.ws_rank_tok[(size_t)v * P + r] = rank_tok[r];
-  for (int z = tid; z < NS; z += W * 64) a.ws_special[(size_t)v * NS + z] = spec[z];
+  for (int r = tid; r < P; r += W * 64) a.ws_rank_tok[(size_t)vs * P + r] = rank_tok[r];
+  for (int z = tid; z < NS; z += W * 64) a.ws_special[(size_t)vs * NS + z] = spec[z];
   if (bad) atomicOr(a.status, (uint32_t)MOE_DEV_STATUS_BAD_EXPERT_ID);
 }
 
