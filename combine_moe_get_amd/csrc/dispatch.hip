@@ -28,21 +28,26 @@
 namespace moe {
 
 // ---- bf16 passthrough --------------------------------------------------------
-// wave gw = (token, slice); slice sl covers 16-byte chunks [64 sl, 64 sl + 64)
-__global__ void __launch_bounds__(256) dispatch_copy_kernel(DispatchArgs a, int nslice) {
-  const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+// one wave per workgroup; wave gw = (token, slice), slice sl covers the 16-byte chunks
+// [128 sl, 128 sl + 128) of the row: lane l copies chunks 128 sl + l and 128 sl + 64 + l.
+// Measured on gfx950 at T=4096, H=7168, top-8 with every input read from HBM: 104.2-104.6 us
+// against 105.6-106.5 us for 1 KB slices in four-wave workgroups.
+__global__ void __launch_bounds__(64) dispatch_copy_kernel(DispatchArgs a, int nslice) {
+  const int lane = threadIdx.x;
+  const int gw = blockIdx.x;
   const int t = gw / nslice, sl = gw - t * nslice;
-  if (t >= a.T) return;  // whole wave
+  if (t >= a.T) return;
   const int K = a.K, H = a.H, nch = H >> 3;
 
   // the slice is requested together with the slot rows (not after them): one load latency
   // less per wave, at the price of reading the slice of a token with no routed copy
   int myrow = -1;
   if (lane < K) myrow = a.dst_row[(size_t)t * K + lane];
-  const int c = lane + 64 * sl;
-  u32x4 v = u32x4{0u, 0u, 0u, 0u};
-  if (c < nch) v = ((const u32x4 *)(a.x + (size_t)t * H))[c];
+  const int c0 = lane + 128 * sl, c1 = c0 + 64;
+  const u32x4 *xr = (const u32x4 *)(a.x + (size_t)t * H);
+  u32x4 v0 = u32x4{0u, 0u, 0u, 0u}, v1 = v0;
+  if (c0 < nch) v0 = xr[c0];
+  if (c1 < nch) v1 = xr[c1];
   uint64_t valid = ballot(myrow >= 0);
   if (valid == 0ull) return;  // masked token, or only special / dropped slots
   const bool write_w = sl == 0 && myrow >= 0 && a.expand_w;
@@ -50,8 +55,9 @@ __global__ void __launch_bounds__(256) dispatch_copy_kernel(DispatchArgs a, int 
   while (valid) {
     const int j = __builtin_ctzll(valid);
     valid &= valid - 1;
-    const int row = readlane(myrow, j);
-    if (c < nch) __builtin_nontemporal_store(v, (u32x4 *)((uint16_t *)a.expand_x + (size_t)row * H) + c);
+    u32x4 *dst = (u32x4 *)((uint16_t *)a.expand_x + (size_t)readlane(myrow, j) * H);
+    if (c0 < nch) __builtin_nontemporal_store(v0, dst + c0);
+    if (c1 < nch) __builtin_nontemporal_store(v1, dst + c1);
   }
   if (write_w) a.expand_w[myrow] = a.w ? a.w[(size_t)t * K + lane] : 1.0f;
 }
@@ -180,10 +186,9 @@ hipError_t launch_dispatch(const DispatchArgs &a, int quant_mode, bool per_exper
   if (a.T == 0) return hipSuccess;
   const int nch = a.H / 8;
   if (quant_mode == 0) {
-    const int nslice = (nch + 63) / 64;
+    const int nslice = (nch + 127) / 128;
     const int64_t waves = (int64_t)a.T * nslice;
-    hipLaunchKernelGGL(dispatch_copy_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a,
-                       nslice);
+    hipLaunchKernelGGL(dispatch_copy_kernel, dim3((unsigned)waves), dim3(64), 0, stream, a, nslice);
     return hipGetLastError();
   }
   const int pairs = (nch + 1) / 2;  // <= 512 for H <= 8192
