@@ -11,8 +11,8 @@
 //
 // Work split (measured on gfx950: more, smaller waves keep more HBM traffic
 // in flight than one wave per token holding the whole row):
-//  - bf16 copy: one wave per (token, 1 KB slice of the row); lane l loads one
-//    16-byte chunk and stores it to each of the token's K rows.
+//  - bf16 copy: one wave per (token, 2 KB slice of the row); lane l loads two
+//    16-byte chunks and stores them to each of the token's K rows.
 //  - int8: one workgroup per token, one lane per 16 channels (32 bytes of
 //    bf16 in, 16 bytes of codes out, so every store instruction of a wave
 //    writes 1 KB contiguous); the dynamic scale needs the row's amax: a wave
@@ -20,9 +20,12 @@
 //  - int8 with per-expert scales: one workgroup per token (dynamic) or per
 //    (token, expert-id parity) (static), the copies quantized one at a time (see
 //    dispatch_quant_expert_kernel).
-// Loads are ordinary (the row is read once, K stores reuse it from VGPRs);
-// stores are non-temporal: receive rows are written once and read by a later
-// kernel.
+// Loads are ordinary (the row is read once, K stores reuse it from VGPRs).
+// Receive rows are written once and read by a later kernel: the int8 codes are
+// stored non-temporally, the bf16 copies of dispatch_copy_kernel with the sc1
+// policy (row_store_sc1), whichever measured faster for each (the single-launch
+// layout + dispatch kernel, for batches of at most 8192 slots, keeps
+// non-temporal stores for both).
 #include "dispatch_dev.hpp"
 
 namespace moe {
@@ -30,8 +33,8 @@ namespace moe {
 // ---- bf16 passthrough --------------------------------------------------------
 // one wave per workgroup; wave gw = (token, slice), slice sl covers the 16-byte chunks
 // [128 sl, 128 sl + 128) of the row: lane l copies chunks 128 sl + l and 128 sl + 64 + l.
-// Measured on gfx950 at T=4096, H=7168, top-8 with every input read from HBM: 104.2-104.6 us
-// against 105.6-106.5 us for 1 KB slices in four-wave workgroups.
+// Measured on gfx950 at T=4096, H=7168, top-8 with every input read from HBM (non-temporal
+// stores then): 104.2-104.6 us against 105.6-106.5 us for 1 KB slices in four-wave workgroups.
 __global__ void __launch_bounds__(64) dispatch_copy_kernel(DispatchArgs a, int nslice) {
   const int lane = threadIdx.x;
   const int gw = blockIdx.x;
@@ -55,9 +58,9 @@ __global__ void __launch_bounds__(64) dispatch_copy_kernel(DispatchArgs a, int n
   while (valid) {
     const int j = __builtin_ctzll(valid);
     valid &= valid - 1;
-    u32x4 *dst = (u32x4 *)((uint16_t *)a.expand_x + (size_t)readlane(myrow, j) * H);
-    if (c0 < nch) __builtin_nontemporal_store(v0, dst + c0);
-    if (c1 < nch) __builtin_nontemporal_store(v1, dst + c1);
+    void *dst = (uint16_t *)a.expand_x + (size_t)readlane(myrow, j) * H;
+    if (c0 < nch) row_store_sc1(v0, dst, 2 * H, c0 * 16);
+    if (c1 < nch) row_store_sc1(v1, dst, 2 * H, c1 * 16);
   }
   if (write_w) a.expand_w[myrow] = a.w ? a.w[(size_t)t * K + lane] : 1.0f;
 }

@@ -65,6 +65,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (bf16_rne_hi(lo) >> 16) | bf16_rne_hi(hi);
 }
 
+// ---- row stores ----------------------------------------------------------------
+
+// 16-byte store at byte offset `off` of a row of `row_bytes` bytes that starts at `row`, a
+// wave-uniform address (the buffer resource lives in scalar registers), with the "sc1" cache
+// policy and no "nt" hint.  Used for the bf16 receive rows: measured on gfx950 at T=4096,
+// H=7168, top-8 with ten rotating input and output sets (no reuse through the 256 MB
+// Infinity Cache), 104 -> 101.5 us against non-temporal stores.  The int8 dispatch (57.9 ->
+// 60.5 us) and the combine's output rows (90.2 -> 91.5 us) measured slower with it and keep
+// non-temporal stores; with only four output sets (235 MB, which the Infinity Cache holds)
+// the combine had looked faster with it (89.6 -> 88.1 us).  An offset at or past row_bytes
+// is dropped by the buffer range check.
+__device__ __forceinline__ void row_store_sc1(u32x4 v, void *row, int row_bytes, int off) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(row, (short)0, row_bytes, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 16 /* sc1 */);
+}
+
 // ---- kernel argument blocks -----------------------------------------------
 
 struct LayoutArgs {
