@@ -6,21 +6,25 @@
 // rank r owns experts [rL, rL + L) (DeepEP issue "#84 Questions on Profiling
 // dispatch_t ...", the masking snippet).  Two launches:
 //
-//  1. count (one workgroup per source rank = one chunk of BS tokens): the
-//     chunk's ids are staged in LDS once; a slot-parallel pass (one lane per
-//     slot) finds owners, specials and bad ids; per-wave histograms in LDS are
-//     built with a "match" of the 64 slots of a wave by expert id (ballots
-//     over the id bits, or for large chunks per-wave LDS tables of lane
-//     masks), so a wave ranks 64 slots in order; a scan over the waves turns them into
-//     chunk-local stable ranks (kept in dst_row), recv_counts[:, s] (and its
-//     transpose in the workspace), is_token_in_rank rows and per-chunk
-//     rank / special counts.
+//  1. count (one workgroup per source rank's chunk of BS tokens, or per
+//     sub-chunk of at most 128 tokens where a larger chunk is split, see
+//     layout_subchunks): the sub-chunk's ids are staged in LDS once; a
+//     slot-parallel pass (one lane per slot) finds owners, specials and bad
+//     ids; per-wave histograms in LDS are built with a "match" of the 64 slots
+//     of a wave by expert id (ballots over the id bits, or for large chunks
+//     per-wave LDS tables of lane masks), so a wave ranks 64 slots in order; a
+//     scan over the waves turns them into sub-chunk-local stable ranks (kept in
+//     dst_row), the sub-chunk's per-expert counts (a row of the workspace count
+//     matrix; recv_counts[:, s] directly when the chunk is not split),
+//     is_token_in_rank rows and per-sub-chunk rank / special counts.
 //  2. scan + finalize (one workgroup per source rank): each reduces the
-//     [P][E] count matrix with all loads in flight at once, scans the expert
-//     totals into offsets and writes dst_row = first row of (s, e) + local
-//     rank and src_info for its chunk; workgroup s also writes
-//     num_tokens_per_rank[s] and the totals of special ids s, s + P, ...
-//     (their inputs loaded at the start), workgroup 0 the per-expert outputs.
+//     [P m][E] count matrix (m sub-chunks per chunk) with all loads in flight
+//     at once, scans the expert totals into offsets and writes dst_row = first
+//     row of (s, e) + the counts of the chunk's earlier sub-chunks + local rank
+//     and src_info for its chunk (and recv_counts[:, s] when the chunk is
+//     split); workgroup s also writes num_tokens_per_rank[s] and the totals of
+//     special ids s, s + P, ... (their inputs loaded at the start), workgroup 0
+//     the per-expert outputs.
 //
 // Small worlds (T * K <= 8192 slots) take one launch instead
 // (layout_fused_kernel, below), optionally followed in the same kernel by the
