@@ -53,21 +53,27 @@ __global__ void __launch_bounds__(64) combine_kernel(CombineArgs a, int nslice) 
   const int cb = sl * 64 * U + lane;
   u32x4 *o = (u32x4 *)(a.out + (size_t)t * H);
 
-  if (a.mask && !a.mask[t]) {
+  // the token's mask byte and its slots' ids, weights and rows are requested together, so
+  // the wave waits out one load latency before its row loads, not three
+  const bool active = !a.mask || a.mask[t];
+  int id = -1, row = -1;
+  float wt = 0.0f;
+  if (lane < K) {
+    id = a.topk_idx[(size_t)t * K + lane];
+    wt = a.w[(size_t)t * K + lane];
+    row = a.dst_row[(size_t)t * K + lane];
+  }
+  if (!active) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (cb + 64 * u < nch) __builtin_nontemporal_store((u32x4{0u, 0u, 0u, 0u}), o + cb + 64 * u);
     return;
   }
 
-  int kind = SK_NONE, row = 0, ci = 0;
-  float wt = 0.0f;
+  int kind = SK_NONE, ci = 0;
   if (lane < K) {
-    const int id = a.topk_idx[(size_t)t * K + lane];
-    wt = a.w[(size_t)t * K + lane];
     const int zc = a.E + a.Z;
     if (id >= 0 && id < a.E) {
-      row = a.dst_row[(size_t)t * K + lane];
       kind = row >= 0 ? SK_ROUTED : SK_NONE;
     } else if (SPECIAL && id >= zc && id < zc + a.C) {
       kind = SK_COPY;
