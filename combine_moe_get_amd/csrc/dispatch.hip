@@ -20,7 +20,8 @@
 //  - int8 with per-expert scales: one workgroup per token (dynamic) or per
 //    (token, expert-id parity) (static), the copies quantized one at a time (see
 //    dispatch_quant_expert_kernel).
-// Loads are ordinary (the row is read once, K stores reuse it from VGPRs).
+// Loads are ordinary (the row is read once, K stores reuse it from VGPRs; the bf16
+// copy reads through a buffer resource, row_load).
 // Receive rows are written once and read by a later kernel: the int8 codes are
 // stored non-temporally, the bf16 copies of dispatch_copy_kernel with the sc1
 // policy (row_store_sc1), whichever measured faster for each (the single-launch
@@ -47,10 +48,10 @@ __global__ void __launch_bounds__(64) dispatch_copy_kernel(DispatchArgs a, int n
   int myrow = -1;
   if (lane < K) myrow = a.dst_row[(size_t)t * K + lane];
   const int c0 = lane + 128 * sl, c1 = c0 + 64;
-  const u32x4 *xr = (const u32x4 *)(a.x + (size_t)t * H);
+  const uint16_t *xr = a.x + (size_t)t * H;
   u32x4 v0 = u32x4{0u, 0u, 0u, 0u}, v1 = v0;
-  if (c0 < nch) v0 = xr[c0];
-  if (c1 < nch) v1 = xr[c1];
+  if (c0 < nch) v0 = row_load(xr, 2 * H, c0 * 16);
+  if (c1 < nch) v1 = row_load(xr, 2 * H, c1 * 16);
   uint64_t valid = ballot(myrow >= 0);
   if (valid == 0ull) return;  // masked token, or only special / dropped slots
   const bool write_w = sl == 0 && myrow >= 0 && a.expand_w;
