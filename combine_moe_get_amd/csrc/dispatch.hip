@@ -36,6 +36,8 @@ namespace moe {
 // [128 sl, 128 sl + 128) of the row: lane l copies chunks 128 sl + l and 128 sl + 64 + l.
 // Measured on gfx950 at T=4096, H=7168, top-8 with every input read from HBM (non-temporal
 // stores then): 104.2-104.6 us against 105.6-106.5 us for 1 KB slices in four-wave workgroups.
+// With buffer-resource loads and sc1 stores (98-100 us), 1, 3 and 4 KB slices measured
+// 102.6-103.5, 104.7-105.3 and 106.2-106.7 us against 100.1-100.8 us for 2 KB in one run.
 __global__ void __launch_bounds__(64) dispatch_copy_kernel(DispatchArgs a, int nslice) {
   const int lane = threadIdx.x;
   const int gw = blockIdx.x;
