@@ -363,7 +363,13 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
     red_pre[v] = below;
   }
   __syncthreads();
-  if (pre_rt) atomicAdd(&acc_rt, pre_rt);
+  // distinct tokens on rank s: a DPP sum over the wave, then one LDS add per wave (an atomic
+  // add of a per-lane value to one address compiles to a scalar loop over the active lanes:
+  // ~1 us for 32 lanes on gfx950, on the critical path of workgroup wave 0)
+  if (wv * 64 < Pv) {
+    const int wsum_rt = wave_inclusive_sum(pre_rt);  // lane 63: the wave's total
+    if (lane == 63 && wsum_rt) atomicAdd(&acc_rt, wsum_rt);
+  }
   if (pre_sp) atomicAdd(&acc_sp[tid / Pv], pre_sp);
   // columns longer than the workgroup (Pv > 1024) and further special ids (rare)
   for (int i = tid + 1024; i < Pv; i += 1024) atomicAdd(&acc_rt, a.ws_rank_tok[(size_t)i * P + s]);
