@@ -77,16 +77,19 @@ struct SlotLanes {
   }
 };
 
-// lanes whose key equals the calling lane's (keys < 2^nbits): AND over the key bits of
-// (ballot or its complement).  Every lane of the wave must call it.
+// lanes whose key equals the calling lane's (keys < 2^nbits): a lane differs from the calling
+// lane wherever the ballot of a key bit differs from the calling lane's own bit (all ones or
+// all zeros), so the mismatches are ORed up per 32-bit half and complemented at the end.
+// Every lane of the wave must call it.
 __device__ __forceinline__ uint64_t match_key(int key, int nbits) {
-  uint64_t peers = ~0ull;
+  uint32_t mis_lo = 0u, mis_hi = 0u;
   for (int b = 0; b < nbits; ++b) {
-    const bool bit = (key >> b) & 1;
-    const uint64_t bl = ballot(bit);
-    peers &= bit ? bl : ~bl;
+    const uint32_t own = (uint32_t)(__builtin_amdgcn_sbfe(key, b, 1));  // all ones where the lane's bit is set
+    const uint64_t bl = ballot(own != 0u);
+    mis_lo |= (uint32_t)bl ^ own;
+    mis_hi |= (uint32_t)(bl >> 32) ^ own;
   }
-  return peers;
+  return ~(((uint64_t)mis_hi << 32) | mis_lo);
 }
 
 // own >= 0 is the owner rank of the lane's slot: true for the first slot of its token
