@@ -120,6 +120,10 @@ static LayoutArgs layout_sizes(const moe_get_shape_t *shape) {
   const int Sv = a.BSv * K;
   a.Svpad = Sv + (Sv & 1);
   a.Etot = (int64_t)E + NS;
+  a.divL = div_magic(a.L);
+  a.divK = div_magic(K);
+  a.divBSv = div_magic(a.BSv);
+  a.divE = div_magic(E);
   return a;
 }
 

@@ -68,9 +68,9 @@ struct SlotLanes {
   int g, j, per;
   bool on;         // the lane holds a slot
   uint64_t group;  // the lanes of the same token
-  __device__ SlotLanes(int K, int lane) {
-    per = 64 / K;
-    g = lane / K;
+  __device__ SlotLanes(int K, uint32_t divK, int lane) {
+    per = fast_div(64, divK);
+    g = fast_div(lane, divK);
     j = lane - g * K;
     on = g < per;
     group = on ? (((1ull << K) - 1) << (g * K)) : 0ull;  // K <= 16
@@ -186,7 +186,7 @@ __global__ void __launch_bounds__(W * 64) layout_count_kernel(LayoutArgs a) {
     for (int u = 0; u < PER; ++u) {
       const int i = tid + u * W * 64;
       v[u] = i < S ? a.topk_idx[slot0 + i] : 0;
-      on[u] = (i < S && a.mask) ? a.mask[t0 + i / K] : (uint8_t)1;
+      on[u] = (i < S && a.mask) ? a.mask[t0 + fast_div(i, a.divK)] : (uint8_t)1;
     }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -197,7 +197,7 @@ __global__ void __launch_bounds__(W * 64) layout_count_kernel(LayoutArgs a) {
   } else {
     for (int i = tid; i < S; i += W * 64) {
       const int v = a.topk_idx[slot0 + i];
-      ids[i] = (!a.mask || a.mask[t0 + i / K]) ? v : -1;
+      ids[i] = (!a.mask || a.mask[t0 + fast_div(i, a.divK)]) ? v : -1;
     }
   }
   for (int i = tid; i < W * a.Epad / 2; i += W * 64) ((uint32_t *)cnt)[i] = 0u;
@@ -209,7 +209,7 @@ __global__ void __launch_bounds__(W * 64) layout_count_kernel(LayoutArgs a) {
   // ---- token phase (slot-parallel): owner ranks, specials, bad ids ---------
   bool bad = false;
   {
-    const SlotLanes sl(K, lane);
+    const SlotLanes sl(K, a.divK, lane);
     const int nbp = 32 - __builtin_clz((unsigned)P);
     for (int tb = wv * sl.per; tb < nt; tb += W * sl.per) {  // uniform per wave
       const int tl = tb + sl.g;
@@ -222,7 +222,7 @@ __global__ void __launch_bounds__(W * 64) layout_count_kernel(LayoutArgs a) {
         } else if (id >= E) {
           atomicAdd(&spec[id - E], 1);
         } else {
-          own = id / a.L;
+          own = fast_div(id, a.divL);
         }
       }
       if (BIG ? first_of_owner_lds(sl, own, lane, mtab) : first_of_owner(sl, own, nbp, lane)) {
@@ -359,7 +359,7 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
 
   // partial column sums: virtual thread (e, g) sums rows g, g+G, ... of the count matrix
   for (int v = tid; v < E * G; v += 1024) {
-    const int e = v % E, g = v / E;
+    const int g = fast_div(v, a.divE), e = v - g * E;
     int tot = 0, below = 0;
     column_sums(a.ws_cnt_t, E, e, Pv, g, G, s * m, tot, below);
     red_tot[v] = tot;
@@ -430,7 +430,7 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
     basel[e] += offl[e];
     liml[e] = INT32_MAX;
     if (a.rank_stride > 0) {  // move the owner's rows into its window [r A, r A + A)
-      const int r = e / a.L;
+      const int r = fast_div(e, a.divL);
       const int64_t w0 = (int64_t)r * a.rank_stride;
       basel[e] = (int)(w0 + basel[e] - offl[r * a.L]);
       liml[e] = (int)(w0 + a.rank_stride);
@@ -442,7 +442,7 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
   bool overflow = false;
   auto finalize_slot = [&](int i, int v, int e) {  // v: the slot's rank in its sub-chunk, or < 0
     if (v < 0) return;
-    const int qq = SUBS ? (i / K) / a.BSv : 0;
+    const int qq = SUBS ? fast_div(fast_div(i, a.divK), a.divBSv) : 0;
     const int row = basel[e] + (qq > 0 ? subb[(qq - 1) * E + e] : 0) + v;
     if (row >= liml[e]) {  // only a token repeating an expert id can overflow its window
       overflow = true;
@@ -532,7 +532,7 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
   // loads issued before the first barrier, so their latency overlaps the set-up below:
   // this lane's slot of the first pass over all tokens, and the first token this
   // workgroup dispatches
-  const SlotLanes sl(K, lane);
+  const SlotLanes sl(K, a.divK, lane);
   int pre_id = -1;
   bool pre_on = false;
   {
@@ -552,7 +552,7 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
   for (int i = tid; i < W * a.Epad / 2; i += NT) ((uint32_t *)cnt)[i] = 0u;
   for (int i = tid; i < S; i += NT) {  // a slot of an inactive token is stored as -1 (dropped)
     const int v = a.topk_idx[slot0 + i];
-    ids[i] = (!a.mask || a.mask[u0 + i / K]) ? v : -1;
+    ids[i] = (!a.mask || a.mask[u0 + fast_div(i, a.divK)]) ? v : -1;
   }
   zero_bytes(a.itr + (size_t)u0 * P, (size_t)nt * P, tid, NT);
   __syncthreads();
@@ -582,7 +582,7 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
           bad = true;
         } else {
           atomicAdd(&(t < u0 ? hist_lo : (SUB && t < cend) ? hist_mid : hist_hi)[id], 1);
-          if (id < E) own = id / a.L;
+          if (id < E) own = fast_div(id, a.divL);
         }
       }
       if (first) {  // uniform per workgroup
@@ -594,7 +594,7 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
   // ---- this sub-chunk: is_token_in_rank rows --------------------------------------
   for (int i = tid; i < S; i += NT) {
     const int id = ids[i];
-    if (id >= 0 && id < E) a.itr[(size_t)u0 * P + (size_t)(i / K) * P + id / a.L] = 1;
+    if (id >= 0 && id < E) a.itr[(size_t)u0 * P + (size_t)fast_div(i, a.divK) * P + fast_div(id, a.divL)] = 1;
   }
 
   // ---- this sub-chunk: stable ranks inside each wave segment (ballot match) -------
@@ -657,7 +657,7 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
     basel[e] = offl[e] + hist_lo[e];
     liml[e] = INT32_MAX;
     if (a.rank_stride > 0) {  // rank r's rows go to its window [r A, r A + A)
-      const int r = e / a.L;
+      const int r = fast_div(e, a.divL);
       const int64_t w0 = (int64_t)r * a.rank_stride;
       basel[e] = (int)(w0 + basel[e] - offl[r * a.L]);
       liml[e] = (int)(w0 + a.rank_stride);

@@ -108,7 +108,16 @@ struct LayoutArgs {
   int32_t *ws_rank_tok;  // [P m][P]  per sub-chunk: tokens with a copy on rank r
   int32_t *ws_special;   // [P m][NS] per sub-chunk: special slots per id
   int32_t mt;            // 64-bit words per wave of the count kernel's LDS match tables; set by the launcher
+  uint32_t divL, divK, divBSv, divE;  // div_magic of L, K, BSv and E: see fast_div
 };
+
+// Division by a divisor d fixed for the whole call, as a multiply-high: m = div_magic(d) =
+// ceil(2^32 / d) (0 for d = 1) and n / d = umulhi(n, m) for 0 <= n with n d < 2^32 (then
+// n m / 2^32 lies in [n / d, n / d + n / 2^32) and n / 2^32 < 1 / d, so the floor is exact).
+// Every use here divides a lane, an expert id, a slot of a (sub-)chunk or a token of a chunk
+// (all below 2^13) by L, K, E or a sub-chunk size (all at most 2^11).
+inline uint32_t div_magic(int d) { return d > 1 ? (uint32_t)(((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d) : 0u; }
+__device__ __forceinline__ int fast_div(int n, uint32_t m) { return m ? (int)__umulhi((uint32_t)n, m) : n; }
 
 struct DispatchArgs {
   const uint16_t *x;
