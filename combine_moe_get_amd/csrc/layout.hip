@@ -317,13 +317,13 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
   __shared__ int liml[2048];
   __shared__ int offl[2049];
   __shared__ int wsum[16];
+  __shared__ int wsum2[64];
   __shared__ int acc_rt;             // distinct tokens on rank s, summed over the source chunks
   __shared__ int acc_sp[kSpecPerBlock];  // special ids s, s + P, ... summed over the source chunks
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int E = a.E, P = a.P, NS = a.NS, K = a.K;
   const int m = SUBS ? a.m : 1, Pv = P * m;  // sub-chunks per chunk; rows of the workspace matrices
-  const int G = E >= 1024 ? 1 : 1024 / E;  // row groups per expert column
   const int S = a.BS * K;
   const size_t slot0 = (size_t)s * S;
   // loads issued now so their latency overlaps the reduction below: the thread's first SPT
@@ -357,7 +357,9 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
   if (tid == 0) acc_rt = 0;
   if (tid < kSpecPerBlock) acc_sp[tid] = 0;
 
-  // partial column sums: virtual thread (e, g) sums rows g, g+G, ... of the count matrix
+  // partial column sums: virtual thread (e, g) sums rows g, g+G, ... of the count matrix (the
+  // 64 lanes of a wave read 64 neighbouring columns of one row: coalesced)
+  const int G = E >= 1024 ? 1 : 1024 / E;  // row groups per expert column
   for (int v = tid; v < E * G; v += 1024) {
     const int g = fast_div(v, a.divE), e = v - g * E;
     int tot = 0, below = 0;
@@ -365,6 +367,27 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
     red_tot[v] = tot;
     red_pre[v] = below;
   }
+  __syncthreads();
+
+  // expert totals (tot) and the copies sent by the sub-chunks before this chunk (below): thread
+  // t owns expert t (E <= 1024) or experts 2t and 2t + 1 (E > 1024, one row group); then the
+  // exclusive scan of the totals, a wave scan now and the wave totals after the next barrier
+  const bool pairs = E > 1024;
+  const int eg = pairs ? 2 * tid : tid;
+  int tot0 = 0, bel0 = 0, tot1 = 0, bel1 = 0;
+  if (eg < E) {
+    for (int g = 0; g < G; ++g) {
+      tot0 += red_tot[g * E + eg];
+      bel0 += red_pre[g * E + eg];
+    }
+  }
+  if (pairs && eg + 1 < E) {
+    tot1 = red_tot[eg + 1];
+    bel1 = red_pre[eg + 1];
+  }
+  const int local = tot0 + tot1;
+  const int incl = wave_inclusive_sum(local);
+  if (lane == 63) wsum[wv] = incl;
   __syncthreads();
   // distinct tokens on rank s: a DPP sum over the wave, then one LDS add per wave (an atomic
   // add of a per-lane value to one address compiles to a scalar loop over the active lanes:
@@ -378,19 +401,8 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
   for (int i = tid + 1024; i < Pv; i += 1024) atomicAdd(&acc_rt, a.ws_rank_tok[(size_t)i * P + s]);
   for (int e2 = tid + 1024; e2 < Pv * nsp; e2 += 1024)
     atomicAdd(&acc_sp[e2 / Pv], a.ws_special[(size_t)(e2 % Pv) * NS + s + (e2 / Pv) * P]);
-  for (int e = tid; e < E; e += 1024) {
-    int tot = 0, below = 0;
-    for (int g = 0; g < G; ++g) {
-      tot += red_tot[g * E + e];
-      below += red_pre[g * E + e];
-    }
-    totl[e] = tot;
-    basel[e] = below;
-  }
-  __syncthreads();
-
   // recv_counts column s, and the first row of each later sub-chunk relative to the chunk's
-  // (red is free since the barrier above)
+  // (subb aliases red, whose last reads were before the barrier above)
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int e = tid + 1024 * h;
@@ -406,37 +418,37 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
       a.recv_counts[(size_t)e * P + s] = run;
     }
   }
-
-  // exclusive scan of totl[0..E): thread tid owns elements 2tid, 2tid+1
-  const int e0 = 2 * tid, e1 = 2 * tid + 1;
-  const int v0 = e0 < E ? totl[e0] : 0;
-  const int v1 = e1 < E ? totl[e1] : 0;
-  const int local = v0 + v1;
-  const int incl = wave_inclusive_sum(local);
-  if (lane == 63) wsum[wv] = incl;
-  __syncthreads();
   if (wv == 0) {
     const int ws = lane < 16 ? wsum[lane] : 0;
     const int wi = wave_inclusive_sum(ws);
-    if (lane < 16) wsum[lane] = wi - ws;  // exclusive prefix of the wave totals
+    wsum2[lane] = wi - ws;  // exclusive prefix of the wave totals (lanes >= 16 unused)
   }
   __syncthreads();
-  const int excl = incl - local + wsum[wv];
-  if (e0 < E) offl[e0] = excl;
-  if (e1 < E) offl[e1] = excl + v0;
-  if (e0 == E - 1 || e1 == E - 1) offl[E] = excl + local;  // the thread holding element E-1 writes N
+  if (eg < E) {
+    const int excl = incl - local + wsum2[wv];
+    totl[eg] = tot0;
+    offl[eg] = excl;
+    basel[eg] = bel0 + excl;
+    liml[eg] = INT32_MAX;
+    if (eg == E - 1) offl[E] = excl + tot0;  // N
+    if (pairs && eg + 1 < E) {
+      totl[eg + 1] = tot1;
+      offl[eg + 1] = excl + tot0;
+      basel[eg + 1] = bel1 + excl + tot0;
+      liml[eg + 1] = INT32_MAX;
+      if (eg + 1 == E - 1) offl[E] = excl + tot0 + tot1;
+    }
+  }
   __syncthreads();
-  for (int e = tid; e < E; e += 1024) {
-    basel[e] += offl[e];
-    liml[e] = INT32_MAX;
-    if (a.rank_stride > 0) {  // move the owner's rows into its window [r A, r A + A)
+  if (a.rank_stride > 0) {  // move the owner's rows into its window [r A, r A + A) (uniform branch)
+    for (int e = tid; e < E; e += 1024) {
       const int r = fast_div(e, a.divL);
       const int64_t w0 = (int64_t)r * a.rank_stride;
       basel[e] = (int)(w0 + basel[e] - offl[r * a.L]);
       liml[e] = (int)(w0 + a.rank_stride);
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   // rows of this chunk's slots
   bool overflow = false;
