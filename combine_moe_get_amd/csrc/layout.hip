@@ -317,7 +317,6 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
   __shared__ int liml[2048];
   __shared__ int offl[2049];
   __shared__ int wsum[16];
-  __shared__ int wsum2[64];
   __shared__ int acc_rt;             // distinct tokens on rank s, summed over the source chunks
   __shared__ int acc_sp[kSpecPerBlock];  // special ids s, s + P, ... summed over the source chunks
   const int s = blockIdx.x;
@@ -418,14 +417,10 @@ __global__ void __launch_bounds__(1024) layout_scan_finalize_kernel(LayoutArgs a
       a.recv_counts[(size_t)e * P + s] = run;
     }
   }
-  if (wv == 0) {
-    const int ws = lane < 16 ? wsum[lane] : 0;
-    const int wi = wave_inclusive_sum(ws);
-    wsum2[lane] = wi - ws;  // exclusive prefix of the wave totals (lanes >= 16 unused)
-  }
-  __syncthreads();
+  // the exclusive prefix of the wave totals: every wave sums the totals of the waves before it
+  const int wpre = readlane(wave_inclusive_sum(lane < wv ? wsum[lane] : 0), 63);
   if (eg < E) {
-    const int excl = incl - local + wsum2[wv];
+    const int excl = incl - local + wpre;
     totl[eg] = tot0;
     offl[eg] = excl;
     basel[eg] = bel0 + excl;
