@@ -644,33 +644,31 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
     const int incl = wave_inclusive_sum(local);
     if (lane == 63) wsum[wv] = incl;
     __syncthreads();
-    if (wv == 0) {
-      const int ws = lane < W ? wsum[lane] : 0;
-      const int wi = wave_inclusive_sum(ws);
-      if (lane < W) wsum[lane] = wi - ws;
-    }
-    __syncthreads();
-    int run = incl - local + wsum[wv];
+    // the exclusive prefix of the wave totals: every wave sums the totals of the waves before it
+    const int wpre = readlane(wave_inclusive_sum(lane < wv ? wsum[lane] : 0), 63);
+    int run = incl - local + wpre;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int e = tid * PER + u;
-      if (e < E) offl[e] = run;
+      if (e < E) {
+        offl[e] = run;
+        basel[e] = run + hist_lo[e];
+        liml[e] = INT32_MAX;
+      }
       run += v[u];
       if (e == E - 1) offl[E] = run;
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += NT) {
-    basel[e] = offl[e] + hist_lo[e];
-    liml[e] = INT32_MAX;
-    if (a.rank_stride > 0) {  // rank r's rows go to its window [r A, r A + A)
+  if (a.rank_stride > 0) {  // rank r's rows go to its window [r A, r A + A) (uniform branch)
+    for (int e = tid; e < E; e += NT) {
       const int r = fast_div(e, a.divL);
       const int64_t w0 = (int64_t)r * a.rank_stride;
       basel[e] = (int)(w0 + basel[e] - offl[r * a.L]);
       liml[e] = (int)(w0 + a.rank_stride);
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   // ---- rows of this sub-chunk -----------------------------------------------------
   bool overflow = false;
