@@ -213,18 +213,14 @@ __global__ void __launch_bounds__(W * 64) layout_count_kernel(LayoutArgs a) {
     const int nbp = 32 - __builtin_clz((unsigned)P);
     for (int tb = wv * sl.per; tb < nt; tb += W * sl.per) {  // uniform per wave
       const int tl = tb + sl.g;
-      int own = -1;
-      if (sl.on && tl < nt) {
-        const int id = ids[tl * K + sl.j];
-        if (id == -1) {
-        } else if (id < 0 || (int64_t)id >= a.Etot) {
-          bad = true;
-        } else if (id >= E) {
-          atomicAdd(&spec[id - E], 1);
-        } else {
-          own = fast_div(id, a.divL);
-        }
-      }
+      // the slot's class without nested branches: -1 (dropped), a bad id, a special id (one
+      // predicated LDS add) or a routed id (its owner rank)
+      const bool on = sl.on && tl < nt;
+      const int id = on ? ids[on ? tl * K + sl.j : 0] : -1;
+      const unsigned uid = (unsigned)id;
+      bad = bad || (id != -1 && uid >= (unsigned)a.Etot);
+      if (uid - (unsigned)E < (unsigned)NS) atomicAdd(&spec[id - E], 1);
+      const int own = uid < (unsigned)E ? fast_div(id, a.divL) : -1;
       if (BIG ? first_of_owner_lds(sl, own, lane, mtab) : first_of_owner(sl, own, nbp, lane)) {
         a.itr[(size_t)(t0 + tl) * P + own] = 1;
         atomicAdd(&rank_tok[own], 1);
@@ -583,15 +579,11 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
           on = !a.mask || a.mask[t];
         }
       }
-      int own = -1;
-      if (on && id != -1) {
-        if (id < 0 || id >= Etot) {
-          bad = true;
-        } else {
-          atomicAdd(&(t < u0 ? hist_lo : (SUB && t < cend) ? hist_mid : hist_hi)[id], 1);
-          if (id < E) own = fast_div(id, a.divL);
-        }
-      }
+      // the slot's class without nested branches (see the count kernel)
+      const unsigned uid = on ? (unsigned)id : 0xffffffffu;
+      bad = bad || (on && id != -1 && uid >= (unsigned)Etot);
+      if (uid < (unsigned)Etot) atomicAdd(&(t < u0 ? hist_lo : (SUB && t < cend) ? hist_mid : hist_hi)[id], 1);
+      const int own = uid < (unsigned)E ? fast_div(id, a.divL) : -1;
       if (first) {  // uniform per workgroup
         if (first_of_owner(sl, own, nbp, lane)) atomicAdd(&rtok[own], 1);
       }
