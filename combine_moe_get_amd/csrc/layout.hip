@@ -623,7 +623,7 @@ __global__ void __launch_bounds__(W * 64) layout_fused_kernel(LayoutArgs a, Disp
     if (writer) a.recv_counts[(size_t)e * P + s] = SUB ? hist_mid[e] : run;
   }
 
-  // ---- expert offsets: exclusive scan of the totals (each thread 2 * ceil(E / 2NT) experts) ---
+  // ---- expert offsets: exclusive scan of the totals (thread t owns experts 4t ... 4t + 3) ---
   {
     constexpr int PER = 4;  // E <= 2048 with W >= 8: at most 4 experts per thread
     int v[PER], local = 0;
