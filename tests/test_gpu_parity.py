@@ -56,6 +56,18 @@ def test_fuzz_small_worlds(seed):
     G.assert_case(g, o, qm)
 
 
+@pytest.mark.parametrize("H,K", [(6152, 6), (7168, 8)])
+def test_whole_row_combine_path(H, K):
+    # T >= 2048, rows of 7 slices of 2 KB (6144 < H <= 7168; H = 6152 leaves one 16-byte chunk
+    # in the last slice), top-K <= 8 with dropped and duplicate slots, no mask and no special
+    # experts: the combine runs one wave per whole token
+    w = workloads.fuzz_world(777 + H, T=2048, H=H, K=K, E=64, P=4, Z=0, C=0, Kc=0)
+    y_fn = lambda lo, do: workloads.expert_out_normal(lo["num_rows"], H, seed=H)
+    g, o = G.run_case(2048, H, K, 64, 4, 0, 0, 0, w["topk_idx"], None, w["x"], w["topk_weights"], 0, None,
+                      y_fn, label=f"whole-row combine H={H} K={K}")
+    G.assert_case(g, o, 0)
+
+
 @pytest.mark.parametrize("H", [8, 24, 504, 520, 1576, 4104, 8192])
 def test_ragged_hidden_sizes(H):
     w = workloads.fuzz_world(500 + H, H=H, P=4, Z=1, C=1, Kc=1)
