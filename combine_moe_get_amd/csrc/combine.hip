@@ -12,7 +12,10 @@
 // waves keep more reads in flight than one wave walking a whole token.  The
 // slot descriptors (kind, row, weight) are read by lanes 0..K-1 and broadcast
 // to scalar registers, so the slot loop is uniform; a lane issues the 16-byte
-// loads of both its chunks for every routed slot before the first FMA.
+// loads of both its chunks for every routed slot before the first FMA.  One
+// exception: rows of 7 slices (6144 < H <= 7168) with many tokens, no mask and
+// no special experts run one wave per whole token that writes its row last
+// (combine_row_kernel), which measured faster there and only there.
 #include "moe_internal.hpp"
 
 namespace moe {
