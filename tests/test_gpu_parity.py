@@ -68,6 +68,18 @@ def test_whole_row_combine_path(H, K):
     G.assert_case(g, o, 0)
 
 
+@pytest.mark.parametrize("K,masked", [(16, False), (8, True)])
+def test_large_batch_combine_slice_path(K, masked):
+    # T >= 2048 and H = 7168 but top-16 or an active-token mask: the combine keeps one wave per
+    # (token, 2 KB slice)
+    H = 7168
+    w = workloads.fuzz_world(888 + K, T=2048, H=H, K=K, E=64, P=4, Z=0, C=0, Kc=0)
+    y_fn = lambda lo, do: workloads.expert_out_normal(lo["num_rows"], H, seed=K)
+    g, o = G.run_case(2048, H, K, 64, 4, 0, 0, 0, w["topk_idx"], w["mask"] if masked else None, w["x"],
+                      w["topk_weights"], 0, None, y_fn, label=f"slice combine K={K} masked={masked}")
+    G.assert_case(g, o, 0)
+
+
 @pytest.mark.parametrize("H", [8, 24, 504, 520, 1576, 4104, 8192])
 def test_ragged_hidden_sizes(H):
     w = workloads.fuzz_world(500 + H, H=H, P=4, Z=1, C=1, Kc=1)
@@ -383,7 +395,12 @@ def test_two_launch_layout_for_large_worlds(stride):
                                                # 16 waves with tables at 8192 slots per chunk,
                                                (2, 512, 16, 512, 0, 0, 0),
                                                # an odd top-k with special ids
-                                               (8, 256, 6, 96, 2, 1, 1)])
+                                               (8, 256, 6, 96, 2, 1, 1),
+                                               # E > 1024: the scan kernel sums expert pairs per
+                                               # thread; E = 2048 fills all 1024 threads, odd E
+                                               # leaves the last pair half empty
+                                               (4, 512, 8, 2048, 0, 0, 0),
+                                               (3, 512, 8, 1281, 1, 0, 0)])
 def test_two_launch_layout_rank_and_special_totals(P, BS, K, E, Z, C, Kc):
     # per-rank distinct-token and special-id totals of the two-launch layout are summed by the
     # workgroup of rank s (special ids s, s + P, ...): many specials per workgroup, P > 1024;
