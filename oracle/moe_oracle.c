@@ -326,7 +326,8 @@ int orc_dispatch(const orc_shape_t *s, int quant_mode, const uint16_t *x, const 
  *   copy:  Moe(ori_x) = ori_x
  *   const: Moe(ori_x) = alpha1[c] * ori_x + alpha2[c] * v[c]   (element-wise, [Kc, H])
  * out[t] = sum over the token's slots of w[t,j] * Moe_j, in double precision;
- * routed experts read the expert-output row dst_row[t][j]; dropped slots add
+ * routed experts read the expert-output row dst_row[t][j]; dropped slots (and a
+ * routed copy whose dst_row is -1 because its rank window was full, R8) add
  * nothing; a masked token (R3) gets +0.  Products of a binary32 weight and a
  * bf16 value are exact in double, so the only rounding is in the sums. */
 int orc_combine(const orc_shape_t *s, const uint16_t *expert_out, const int32_t *topk_idx,
@@ -346,6 +347,9 @@ int orc_combine(const orc_shape_t *s, const uint16_t *expert_out, const int32_t 
       int c = slot_class(s, mask, t, id);
       double w = (double)topk_weights[(size_t)t * K + j];
       if (c == SLOT_BAD) bad = 1;
+      /* R8: a copy that did not fit its rank window was never sent (dst_row -1), so its
+       * expert returns nothing for it */
+      if (c == SLOT_ROUTED && dst_row[(size_t)t * K + j] < 0) c = SLOT_NONE;
       if (c == SLOT_ROUTED) {
         const uint16_t *y = expert_out + (size_t)dst_row[(size_t)t * K + j] * H;
         for (h = 0; h < H; ++h) o[h] += w * (double)bf16_to_float(y[h]);

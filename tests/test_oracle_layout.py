@@ -64,6 +64,11 @@ def test_page_routing_tables(key):
         hc = g["hand_counted_single_operator"]
         assert got["num_rows"] == hc["num_rows"]
         np.testing.assert_array_equal(got["special_counts"], hc["special_counts"])
+        np.testing.assert_array_equal(got["num_tokens_per_expert"], hc["num_tokens_per_expert"])
+        np.testing.assert_array_equal(got["num_tokens_per_rank"], hc["num_tokens_per_rank"])
+        np.testing.assert_array_equal(np.diff(got["rank_offsets"]), hc["rows_per_rank"])
+        np.testing.assert_array_equal(got["dst_row"][0], hc["dst_row_token_0"])
+        np.testing.assert_array_equal(got["dst_row"][2], hc["dst_row_token_2"])
     # every rank sent the same table: its rows in expert e are spread one block per source rank
     for e in range(sh.num_experts):
         np.testing.assert_array_equal(got["recv_counts"][e], np.full(sh.num_ranks, occ[e]))
@@ -208,6 +213,23 @@ def test_rank_window_hand_case_with_overflow():
     np.testing.assert_array_equal(lay["src_info"], [0, 1, 3, -1])
     assert lay["status"] == 2
     np.testing.assert_array_equal(lay["num_tokens_per_expert"], [3, 1])  # counts describe the routing
+
+
+def test_combine_after_window_overflow_drops_the_copy():
+    # the overflow hand case above: the copy (token 1, slot 0) was never sent, so the combine
+    # adds nothing for it -- token 1 gets w[1, 1] * row 2 only, even though its id is routed
+    sh = oracle.make_shape(2, 8, 2, 2, 2)
+    topk = np.array([[0, 0], [0, 1]], np.int32)
+    lay = oracle.layout(sh, topk, rank_stride=2)
+    # the rows sit behind a sentinel row, so a read of "row -1" would add 0.75 * 1000
+    y_full = workloads.f32_to_bf16_bits(
+        np.array([[1000.0] * 8, [1.0] * 8, [2.0] * 8, [4.0] * 8, [8.0] * 8], np.float32))
+    y = y_full[1:]
+    assert y.flags["C_CONTIGUOUS"] and y.base is not None
+    w = np.array([[0.5, 0.25], [0.75, 0.125]], np.float32)
+    out = oracle.combine(sh, y, topk, w, lay)
+    np.testing.assert_array_equal(out[0], np.full(8, 0.5 * 1.0 + 0.25 * 2.0))
+    np.testing.assert_array_equal(out[1], np.full(8, 0.125 * 4.0))
 
 
 @pytest.mark.parametrize("seed", range(12))

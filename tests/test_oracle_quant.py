@@ -180,3 +180,32 @@ def test_per_expert_smooth_scales():
             q, scale = oracle.quant_token(x[t], s[topk[t, j]])
             row = lay["dst_row"][t, j]
             assert np.array_equal(d["expand_x"][row], q) and d["dynamic_scales"][row] == scale
+
+
+def test_static_dispatch_hand_case_shared_and_per_expert_scales():
+    # quant_mode 1 through the whole dispatch, against codes worked by hand (every product is
+    # exact in binary32; rint ties to even, saturation at 127).  E = 4 experts over P = 2 ranks,
+    # token 0 routed to experts 1 and 3, token 1 to experts 2 and 0, so the expert-major rows are
+    # row 0 = (token 1, expert 0), row 1 = (token 0, expert 1), row 2 = (token 1, expert 2),
+    # row 3 = (token 0, expert 3).
+    sh = oracle.make_shape(2, 4, 2, 4, 2)
+    topk = np.array([[1, 3], [2, 0]], np.int32)
+    x = _bf([[0.5, 1.5, 2.5, -3.0], [10.0, -20.0, 0.25, 100.0]])
+    lay = oracle.layout(sh, topk)
+    np.testing.assert_array_equal(lay["dst_row"], [[1, 3], [2, 0]])
+    # one [H] vector for every copy: token 0 -> 0.5, 3, 1.25, -12; token 1 -> 10, -40, 0.125, 400
+    s = np.array([1.0, 2.0, 0.5, 4.0], np.float32)
+    d = oracle.dispatch(sh, 1, x, lay, smooth=s, topk_idx=topk)
+    np.testing.assert_array_equal(d["expand_x"], [[10, -40, 0, 127], [0, 3, 1, -12], [10, -40, 0, 127],
+                                                  [0, 3, 1, -12]])
+    # [E, H]: each copy takes its expert's row
+    se = np.array([[1, 1, 1, 1], [2, 2, 2, 2], [0.5, 0.5, 0.5, 0.5], [-1, 1, 64, 0.25]], np.float32)
+    d = oracle.dispatch(sh, 1, x, lay, smooth=se, topk_idx=topk)
+    np.testing.assert_array_equal(d["expand_x"], [[10, -20, 0, 100],   # token 1 x expert 0's row
+                                                  [1, 3, 5, -6],       # token 0 x expert 1's row
+                                                  [5, -10, 0, 50],     # token 1 x expert 2's row
+                                                  [0, 2, 127, -1]])    # token 0 x expert 3's row
+    # no scales: CastToInt8 of x itself
+    d = oracle.dispatch(sh, 1, x, lay, topk_idx=topk)
+    np.testing.assert_array_equal(d["expand_x"], [[10, -20, 0, 100], [0, 2, 2, -3], [10, -20, 0, 100],
+                                                  [0, 2, 2, -3]])
