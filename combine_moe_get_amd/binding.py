@@ -259,6 +259,8 @@ def prepare_dispatch(shape, quant_mode, x, dst_row, x_smooth_scale=None, topk_we
                      expand_x=None, dynamic_scales=None, expand_weights=None, rows=None):
     """Checked, marshalled moe_dispatch call; see dispatch()."""
     T, H, K, E = shape.num_tokens, shape.hidden, shape.topk, shape.num_experts
+    if x is None or dst_row is None:
+        raise ValueError("x and dst_row are required")
     cap = max(T * K if rows is None else int(rows), 1)
     dev = x.device
     if expand_x is None:
@@ -278,9 +280,9 @@ def prepare_dispatch(shape, quant_mode, x, dst_row, x_smooth_scale=None, topk_we
         _ptr(topk_weights, "topk_weights", F32, T * K, required=False),
         _ptr(topk_idx, "topk_idx", I32, T * K, required=False),
         _ptr(dst_row, "dst_row", I32, T * K),
-        _ptr(expand_x, "expand_x", BF16 if quant_mode == 0 else (torch.int8,)),
-        _ptr(dynamic_scales, "dynamic_scales", F32, required=False),
-        _ptr(expand_weights, "expand_weights", F32, required=False),
+        _ptr(expand_x, "expand_x", BF16 if quant_mode == 0 else (torch.int8,), cap * H),
+        _ptr(dynamic_scales, "dynamic_scales", F32, cap, required=False),
+        _ptr(expand_weights, "expand_weights", F32, cap, required=False),
         None,
     ]
     keep = (shape, x, dst_row, x_smooth_scale, topk_weights, topk_idx)
@@ -299,22 +301,25 @@ def dispatch(shape, quant_mode, x, dst_row, x_smooth_scale=None, topk_weights=No
 
 
 def prepare_combine(shape, expert_out, topk_idx, topk_weights, dst_row, x_active_mask=None, ori_x=None,
-                    const_alpha1=None, const_alpha2=None, const_v=None, out=None):
+                    const_alpha1=None, const_alpha2=None, const_v=None, out=None, rows=None):
     """Checked, marshalled moe_combine call; see combine()."""
     T, H, K = shape.num_tokens, shape.hidden, shape.topk
+    special = shape.copy_expert_num + shape.const_expert_num > 0
+    kc = shape.const_expert_num
+    rows = T * K if rows is None else int(rows)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=topk_idx.device)
     args = [
         ctypes.byref(shape),
-        _ptr(expert_out, "expert_out", BF16),
+        _ptr(expert_out, "expert_out", BF16, rows * H, required=T > 0),
         _ptr(topk_idx, "topk_idx", I32, T * K),
         _ptr(topk_weights, "topk_weights", F32, T * K),
         _ptr(x_active_mask, "x_active_mask", U8, T, required=False),
         _ptr(dst_row, "dst_row", I32, T * K),
-        _ptr(ori_x, "ori_x", BF16, T * H, required=False),
-        _ptr(const_alpha1, "const_alpha1", BF16, required=False),
-        _ptr(const_alpha2, "const_alpha2", BF16, required=False),
-        _ptr(const_v, "const_v", BF16, required=False),
+        _ptr(ori_x, "ori_x", BF16, T * H, required=special and T > 0),
+        _ptr(const_alpha1, "const_alpha1", BF16, kc * H, required=kc > 0 and T > 0),
+        _ptr(const_alpha2, "const_alpha2", BF16, kc * H, required=kc > 0 and T > 0),
+        _ptr(const_v, "const_v", BF16, kc * H, required=kc > 0 and T > 0),
         _ptr(out, "out", BF16, T * H),
         None,
     ]
@@ -324,10 +329,12 @@ def prepare_combine(shape, expert_out, topk_idx, topk_weights, dst_row, x_active
 
 
 def combine(shape, expert_out, topk_idx, topk_weights, dst_row, x_active_mask=None, ori_x=None,
-            const_alpha1=None, const_alpha2=None, const_v=None, out=None, stream=None):
-    """moe_combine.  Returns out [T, H] bf16."""
+            const_alpha1=None, const_alpha2=None, const_v=None, out=None, stream=None, rows=None):
+    """moe_combine.  Returns out [T, H] bf16.  `rows` is the number of receive rows expert_out
+    must hold (default T * K, which covers every compact layout; a fixed-capacity layout needs
+    P * rank_stride; a caller that knows N may pass rows=N)."""
     return prepare_combine(shape, expert_out, topk_idx, topk_weights, dst_row, x_active_mask, ori_x,
-                           const_alpha1, const_alpha2, const_v, out)(stream)
+                           const_alpha1, const_alpha2, const_v, out, rows)(stream)
 
 
 def _smooth_rows(shape, x_smooth_scale):

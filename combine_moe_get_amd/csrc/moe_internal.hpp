@@ -32,10 +32,26 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-// wave-wide max through DPP row shifts (device library reduction); exact for any
-// finite values, the result is uniform across the wave
-extern "C" __device__ float __ockl_wfred_max_f32(float);
-__device__ __forceinline__ float wave_max(float v) { return __ockl_wfred_max_f32(v); }
+// wave-wide max over the 64 lanes, returned to every lane.  A running max with DPP moves:
+// shifts by 1, 2, 4, 8 lanes inside each row of 16 leave the row's max in its lane 15; lane 15
+// of rows 0 / 2 is folded into rows 1 / 3 and lane 31 into rows 2 / 3, so lane 63 holds the max
+// of all lanes, which readlane broadcasts.  A lane whose DPP source lies outside its row, or whose
+// row is masked off, keeps its own value (the `old` operand).  max is exact, so the order of the
+// folds does not matter; inputs are finite.  Every lane of the wave must call it.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_fold_max(float v) {
+  const int b = __float_as_int(v);
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(b, b, CTRL, ROW_MASK, 0xf, false)));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = dpp_fold_max<0x111, 0xf>(v);  // row_shr:1
+  v = dpp_fold_max<0x112, 0xf>(v);  // row_shr:2
+  v = dpp_fold_max<0x114, 0xf>(v);  // row_shr:4
+  v = dpp_fold_max<0x118, 0xf>(v);  // row_shr:8
+  v = dpp_fold_max<0x142, 0xa>(v);  // row_bcast:15 -> rows 1, 3
+  v = dpp_fold_max<0x143, 0xc>(v);  // row_bcast:31 -> rows 2, 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
 
 // inclusive prefix sum over the 64 lanes with DPP moves (no LDS round trips): shifts by
 // 1, 2, 4, 8 lanes inside each row of 16, then lane 15 of rows 0 / 2 into rows 1 / 3 and

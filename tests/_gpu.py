@@ -103,7 +103,7 @@ def run_case(T, H, K, E, P, Z, C, Kc, topk, mask, x, weights, quant_mode, smooth
     ex, ds, _ = mg.dispatch(shape, quant_mode, dev(x), lay.dst_row, dev(smooth), wd, tk, expand_weights=ew,
                             rows=cap)
     Yd = dev(Y if Y.shape[0] > 0 else np.zeros((1, H), np.uint16))
-    out = mg.combine(shape, Yd, tk, wd, lay.dst_row, mk, dev(ori_x), dev(a1), dev(a2), dev(v))
+    out = mg.combine(shape, Yd, tk, wd, lay.dst_row, mk, dev(ori_x), dev(a1), dev(a2), dev(v), rows=Yd.shape[0])
     torch.cuda.synchronize()
     g = layout_to_numpy(lay, rank_stride)
     o = dict(lo)
