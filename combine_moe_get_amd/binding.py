@@ -100,6 +100,10 @@ def lib():
         L.moe_get_layout.restype = ctypes.c_int
         L.moe_get_layout_ex.argtypes = [SP, I64] + [V] * 12 + [V, SZ, V]
         L.moe_get_layout_ex.restype = ctypes.c_int
+        L.moe_get_layout_noalloc.argtypes = [SP, I64] + [V] * 12 + [V]
+        L.moe_get_layout_noalloc.restype = ctypes.c_int
+        L.moe_get_noalloc_scratch_bytes.argtypes = []
+        L.moe_get_noalloc_scratch_bytes.restype = SZ
         L.moe_get_rank_capacity.argtypes = [SP]
         L.moe_get_rank_capacity.restype = I64
         L.moe_get_layout_launches.argtypes = [SP]
@@ -246,6 +250,47 @@ def prepare_layout(shape, topk_idx, x_active_mask=None, out=None, workspace=None
     ]
     return PreparedCall(lib().moe_get_layout_ex, args, "moe_get_layout",
                         (shape, topk_idx, x_active_mask, workspace), out)
+
+
+def noalloc_scratch_bytes():
+    """Bytes of the static device scratch behind moe_get_layout_noalloc."""
+    return lib().moe_get_noalloc_scratch_bytes()
+
+
+def prepare_layout_noalloc(shape, topk_idx, x_active_mask=None, out=None, rank_stride=0):
+    """Checked, marshalled moe_get_layout_noalloc call (no workspace argument); see
+    layout_noalloc().  `out` must be given by callers that cannot allocate."""
+    st = check_shape(shape)
+    if st != MOE_OK:
+        raise MoeGetError("layout_noalloc", st)
+    T, K = shape.num_tokens, shape.topk
+    out = out if out is not None else alloc_layout(shape, topk_idx.device, rank_stride)
+    rows = shape.num_ranks * rank_stride if rank_stride > 0 else T * K
+    args = [
+        ctypes.byref(shape), ctypes.c_int64(int(rank_stride)),
+        _ptr(topk_idx, "topk_idx", I32, T * K),
+        _ptr(x_active_mask, "x_active_mask", U8, T, required=False),
+        _ptr(out.num_tokens_per_expert, "num_tokens_per_expert", I32, shape.num_experts),
+        _ptr(out.expert_offsets, "expert_offsets", I32, shape.num_experts + 1),
+        _ptr(out.recv_counts, "recv_counts", I32, shape.num_experts * shape.num_ranks),
+        _ptr(out.special_counts, "special_counts", I32, shape.n_special, required=shape.n_special > 0),
+        _ptr(out.num_tokens_per_rank, "num_tokens_per_rank", I32, shape.num_ranks),
+        _ptr(out.rank_offsets, "rank_offsets", I32, shape.num_ranks + 1),
+        _ptr(out.is_token_in_rank, "is_token_in_rank", U8, T * shape.num_ranks),
+        _ptr(out.dst_row, "dst_row", I32, T * K),
+        _ptr(out.src_info, "src_info", I32, rows),
+        _ptr(out.status, "status", I32, 1),
+        None,
+    ]
+    return PreparedCall(lib().moe_get_layout_noalloc, args, "moe_get_layout_noalloc",
+                        (shape, topk_idx, x_active_mask), out)
+
+
+def layout_noalloc(shape, topk_idx, x_active_mask=None, out=None, stream=None, rank_stride=0):
+    """moe_get_layout_noalloc: the layout of layout(), its workspace in the library's static
+    device scratch (no allocation in the library; raises MoeGetError with status -6 when the
+    shape needs more than noalloc_scratch_bytes())."""
+    return prepare_layout_noalloc(shape, topk_idx, x_active_mask, out, rank_stride)(stream)
 
 
 def layout(shape, topk_idx, x_active_mask=None, out=None, workspace=None, stream=None, rank_stride=0):

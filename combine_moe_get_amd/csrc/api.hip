@@ -1,6 +1,7 @@
 // api.hip -- the extern "C" entry points of libmoe_get: argument checks on
 // the host, then kernel launches on the caller's stream.  Nothing here
-// allocates, synchronizes or keeps state.
+// allocates or synchronizes; the only state is the per-device address of the
+// static scratch of moe_get_layout_noalloc, looked up once per device.
 //
 // Shape limits come from the Constraints section of the CANN
 // "low_latency_dispatch" page (K, BS, H, local_expert_num * ep_world_size)
@@ -8,6 +9,8 @@
 // checked before the call); the kernels add H % 8 == 0, H <= 8192 and at most
 // 1024 special ids.
 #include <string.h>
+
+#include <mutex>
 
 #include "moe_internal.hpp"
 
@@ -65,6 +68,42 @@ WsLayout ws_layout(const moe_get_shape_t *s) {
   return w;
 }
 
+// ---- static scratch of the allocation-free layout entry point ------------------------------
+// The workspace of moe_get_layout_noalloc: the per-sub-chunk count matrices that the two-launch
+// layout's count kernel writes and its scan kernel reads, and the status word used when the caller
+// passes none.  Every element the scan kernel reads is written first by the count kernel of the
+// same call, so nothing has to be cleared between calls.  Each device holds its own copy for the life of
+// the process; calls that overlap on one device share it and race.  In host code `scratch` names a
+// host-side stand-in: kernels get the device address from hipGetSymbolAddress (scratch_on), never
+// the name.
+constexpr size_t kScratchBytes = (size_t)MOE_GET_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_addr[kMaxDevices];  // device address of `scratch` per device, looked up once
+
+// device address of the scratch array on the device that runs `stream` (its first use on a device
+// makes that device current for the lookup, then restores the caller's device)
+int scratch_on(hipStream_t stream, void **out) {
+  int cur = -1, dev = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return MOE_ERR_HIP;
+  dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_addr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return MOE_ERR_HIP;
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return MOE_ERR_HIP;
+    if (e != hipSuccess || !p || ((uintptr_t)p & (kAlign - 1)) != 0) return MOE_ERR_HIP;
+    scratch_addr[dev] = p;
+  }
+  *out = scratch_addr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -79,6 +118,9 @@ const char *moe_get_status_string(int status) {
     case MOE_ERR_CAPACITY: return "tokens per rank exceed num_max_dispatch_tokens_per_rank";
     case MOE_ERR_UNSUPPORTED: return "shape not supported by the kernels (hidden % 8, hidden > 8192 or > 1024 special ids)";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_SCRATCH:
+      return "the layout's workspace for this shape exceeds the static scratch of moe_get_layout_noalloc "
+             "(MOE_GET_NOALLOC_SCRATCH_BYTES); use moe_get_layout_ex with a workspace";
     default: return "unknown status";
   }
 }
@@ -255,6 +297,28 @@ int moe_get_layout_ex(const moe_get_shape_t *shape, int64_t rank_stride, const i
   if (st != MOE_OK) return st;
   return launch_layout(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
+
+int moe_get_layout_noalloc(const moe_get_shape_t *shape, int64_t rank_stride, const int32_t *topk_idx,
+                           const uint8_t *x_active_mask, int32_t *num_tokens_per_expert,
+                           int32_t *expert_offsets, int32_t *recv_counts, int32_t *special_counts,
+                           int32_t *num_tokens_per_rank, int32_t *rank_offsets,
+                           uint8_t *is_token_in_rank, int32_t *dst_row, int32_t *src_info,
+                           uint32_t *status_dev, void *stream) {
+  const int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (ws_layout(shape).total > kScratchBytes) return MOE_ERR_SCRATCH;
+  void *ws = nullptr;
+  const int sst = scratch_on((hipStream_t)stream, &ws);
+  if (sst != MOE_OK) return sst;
+  LayoutArgs a;
+  const int ast = layout_args(shape, rank_stride, topk_idx, x_active_mask, num_tokens_per_expert, expert_offsets,
+                              recv_counts, special_counts, num_tokens_per_rank, rank_offsets, is_token_in_rank,
+                              dst_row, src_info, status_dev, ws, kScratchBytes, a);
+  if (ast != MOE_OK) return ast;
+  return launch_layout(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+size_t moe_get_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int moe_dispatch(const moe_get_shape_t *shape, int32_t quant_mode, const uint16_t *x,
                  const float *x_smooth_scale, int32_t smooth_rows, const float *topk_weights,

@@ -18,7 +18,8 @@
  * Conventions for every entry point
  *  - All array arguments are device pointers (HIP global memory), row-major,
  *    contiguous, allocated and owned by the caller.  The library allocates
- *    nothing and keeps no state between calls.
+ *    nothing and keeps no state between calls (moe_get_layout_noalloc's static
+ *    scratch holds nothing a later call reads).
  *  - bf16 tensors are passed as uint16_t bit patterns.
  *  - `stream` is a hipStream_t (NULL = the default stream).  All work is
  *    enqueued on it in order; no call synchronizes the host.  Calls on
@@ -68,7 +69,8 @@ typedef enum moe_get_status {
   MOE_ERR_SHAPE = -2,       /* sizes outside the Constraints section */
   MOE_ERR_CAPACITY = -3,    /* BS > num_max_dispatch_tokens_per_rank, or a rank window below capacity */
   MOE_ERR_UNSUPPORTED = -4, /* allowed by the page but not by these kernels (H % 8, H > 8192, Z+C+Kc > 1024) */
-  MOE_ERR_HIP = -5          /* the HIP runtime refused a launch */
+  MOE_ERR_HIP = -5,         /* the HIP runtime refused a launch (or a device lookup) */
+  MOE_ERR_SCRATCH = -6      /* moe_get_layout_noalloc: the shape needs more than its static scratch */
 } moe_get_status_t;
 
 /* Bits of the device status word written by moe_get_layout (sticky: the
@@ -157,6 +159,29 @@ int moe_get_layout_ex(const moe_get_shape_t *shape, int64_t rank_stride, const i
                       int32_t *num_tokens_per_rank, int32_t *rank_offsets,
                       uint8_t *is_token_in_rank, int32_t *dst_row, int32_t *src_info,
                       uint32_t *status_dev, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of the static device scratch of moe_get_layout_noalloc (per device). */
+#define MOE_GET_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+/* moe_get_layout_ex without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Results are those of moe_get_layout_ex(shape, rank_stride, ...) bit for bit.  Its workspace
+ * is a static device array of MOE_GET_NOALLOC_SCRATCH_BYTES that every device holds for the
+ * life of the process (moe_get_workspace_size(shape) must fit in it, else MOE_ERR_SCRATCH and
+ * nothing is launched); it allocates nothing and keeps nothing that a later call depends on.
+ * Calls that overlap on one device (concurrent streams, or several host threads) share that
+ * device's scratch and race: order them on one stream.  The first call on a device looks up the
+ * array's device address once (with that device made current); the device is the one of
+ * `stream` (the current device for a NULL stream). */
+int moe_get_layout_noalloc(const moe_get_shape_t *shape, int64_t rank_stride, const int32_t *topk_idx,
+                           const uint8_t *x_active_mask, int32_t *num_tokens_per_expert,
+                           int32_t *expert_offsets, int32_t *recv_counts, int32_t *special_counts,
+                           int32_t *num_tokens_per_rank, int32_t *rank_offsets,
+                           uint8_t *is_token_in_rank, int32_t *dst_row, int32_t *src_info,
+                           uint32_t *status_dev, void *stream);
+
+/* MOE_GET_NOALLOC_SCRATCH_BYTES, for bindings that cannot read the macro. */
+size_t moe_get_noalloc_scratch_bytes(void);
 
 /* Dispatch: quantize (optionally) and scatter every routed copy of every
  * token into its receive row (the alltoallv of quant_out of the Formula, and
