@@ -23,6 +23,7 @@ import hashlib
 import json
 import os
 import re
+import subprocess
 import sys
 import time
 
@@ -124,37 +125,136 @@ def hbm_probe(dev, nbytes=2 << 30, reps=5):
                 kernels="torch fill_ (its vectorized elementwise kernel) / copy_ (hipMemcpy device to device)")
 
 
-def cpu_baseline(inp, target_seconds):
-    """The oracle, as it stands (single-threaded C), timed on this host over whole
-    layout + dispatch + combine passes of the same workload."""
+def cpu_model_name():
+    """The host CPU's model name as lscpu prints it (falls back to /proc/cpuinfo)."""
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for ln in out.splitlines():
+            if ln.startswith("Model name:"):
+                return ln.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        return ""
+
+
+def host_threads():
+    """Worker threads for the all-cores oracle leg: the cores this process may run on, at most
+    16 (the host share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _oracle_pass(inp, lo_only=False):
+    """One single-threaded oracle pass (layout + dispatch + combine); returns (seconds, comm bytes,
+    layout) -- the expert stand-in between dispatch and combine is built outside the timing."""
     import oracle
 
     c = inp["cfg"]
     sh = oracle.make_shape(c["T"], c["H"], c["K"], c["E"], c["P"], c["Z"], c["C"], c["Kc"], c["num_max"])
-    reps, total_comm, dt = 0, 0, 0.0
-    while dt < target_seconds:
+    a = time.perf_counter()
+    lo = oracle.layout(sh, inp["topk_idx"], inp["mask"])
+    oracle.dispatch(sh, c["quant_mode"], inp["x"], lo, smooth=inp["smooth"], topk_idx=inp["topk_idx"])
+    b = time.perf_counter()
+    y = np.ascontiguousarray(inp["x"][lo["src_info"] // c["K"]])  # expert stand-in, not timed
+    e0 = time.perf_counter()
+    oracle.combine(sh, y, inp["topk_idx"], inp["topk_weights"], lo, inp["mask"], inp["ori_x"],
+                   inp["alpha1"], inp["alpha2"], inp["const_v"])
+    dt = (b - a) + (time.perf_counter() - e0)
+    n = lo["num_rows"]
+    return dt, dispatch_comm_bytes(n, c["H"], c["quant_mode"]) + combine_comm_bytes(n, c["H"])
+
+
+def _oracle_threaded_pass(inp, nthreads, return_outputs=False):
+    """The same pass with the oracle's dispatch and combine run by nthreads host threads, each on
+    its own slice of tokens (both are independent per token; the C functions are called
+    unchanged on the slice, and ctypes releases the interpreter lock during each call).  The
+    layout -- a scan over all tokens -- stays single-threaded.  Returns (seconds, comm bytes)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    c = inp["cfg"]
+    T, H, K = c["T"], c["H"], c["K"]
+    sh = oracle.make_shape(T, H, K, c["E"], c["P"], c["Z"], c["C"], c["Kc"], c["num_max"])
+    L = oracle.lib()
+    arr = lambda a, dt: None if a is None else np.ascontiguousarray(a, dtype=dt)
+    x = arr(inp["x"], np.uint16)
+    topk = arr(inp["topk_idx"], np.int32)
+    w = arr(inp["topk_weights"], np.float32)
+    mask = arr(inp["mask"], np.uint8)
+    smooth = arr(inp["smooth"], np.float32)
+    ori, a1, a2, cv = (arr(inp[k], np.uint16) for k in ("ori_x", "alpha1", "alpha2", "const_v"))
+    bounds = np.linspace(0, T, nthreads + 1).astype(np.int64)
+    qm = c["quant_mode"]
+
+    def ptr(a, off_elems=0):
+        return None if a is None else ctypes.c_void_p(a.ctypes.data + int(off_elems) * a.itemsize)
+
+    with ThreadPoolExecutor(nthreads) as pool:
         a = time.perf_counter()
-        lo = oracle.layout(sh, inp["topk_idx"], inp["mask"])
-        oracle.dispatch(sh, c["quant_mode"], inp["x"], lo, smooth=inp["smooth"], topk_idx=inp["topk_idx"])
-        b = time.perf_counter()
-        y = np.ascontiguousarray(inp["x"][lo["src_info"] // c["K"]])  # expert stand-in, not timed
-        e0 = time.perf_counter()
-        oracle.combine(sh, y, inp["topk_idx"], inp["topk_weights"], lo, inp["mask"], inp["ori_x"],
-                       inp["alpha1"], inp["alpha2"], inp["const_v"])
-        dt += (b - a) + (time.perf_counter() - e0)
+        lo = oracle.layout(sh, topk, mask)
         n = lo["num_rows"]
-        total_comm += dispatch_comm_bytes(n, c["H"], c["quant_mode"]) + combine_comm_bytes(n, c["H"])
-        reps += 1
-    model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
-    except OSError:
-        pass
-    return dict(value=round(total_comm / 1e9 / dt, 3), unit="GB/s", cores=1, kind="oracle", cpu_model=model,
-                sample=f"{reps} whole passes (layout + dispatch + combine) of the timed workload, "
-                       f"{dt:.1f} s single-threaded; oracle combine in float64",
-                seconds_per_pass=round(dt / reps, 4))
+        dst = np.ascontiguousarray(lo["dst_row"], np.int32)
+        ex = np.zeros((max(n, 1), H), np.uint16 if qm == 0 else np.int8)
+        ds = np.zeros(max(n, 1), np.float32)
+        ew = np.zeros(max(n, 1), np.float32)
+        srows = 0 if smooth is None else (1 if smooth.size == H else c["E"])
+
+        def disp(i):
+            t0, t1 = int(bounds[i]), int(bounds[i + 1])
+            cs = oracle._CShape(*[int(v) for v in sh._replace(num_tokens=t1 - t0)])
+            return L.orc_dispatch(ctypes.byref(cs), qm, ptr(x, t0 * H), ptr(smooth), srows, None,
+                                  ptr(topk, t0 * K), ptr(dst, t0 * K), ptr(ex), ptr(ds), ptr(ew))
+
+        assert all(r == 0 for r in pool.map(disp, range(nthreads)))
+        b = time.perf_counter()
+        y = np.ascontiguousarray(x[lo["src_info"] // K])  # expert stand-in, not timed
+        out = np.zeros((T, H), np.float64)
+
+        def comb(i):
+            t0, t1 = int(bounds[i]), int(bounds[i + 1])
+            cs = oracle._CShape(*[int(v) for v in sh._replace(num_tokens=t1 - t0)])
+            return L.orc_combine(ctypes.byref(cs), ptr(y if y.size else np.zeros((1, H), np.uint16)),
+                                 ptr(topk, t0 * K), ptr(w, t0 * K), ptr(mask, t0), ptr(dst, t0 * K),
+                                 ptr(ori, t0 * H), ptr(a1), ptr(a2), ptr(cv), ptr(out, t0 * H))
+
+        e0 = time.perf_counter()
+        list(pool.map(comb, range(nthreads)))
+        dt = (b - a) + (time.perf_counter() - e0)
+    if return_outputs:
+        return lo, ex[:n], ds[:n], out
+    return dt, dispatch_comm_bytes(n, H, qm) + combine_comm_bytes(n, H)
+
+
+def cpu_baseline(inp, target_seconds):
+    """The oracle, as it stands, timed on this host over whole layout + dispatch + combine passes of
+    the same workload: single-threaded (the baseline proper: at least 3 passes and about
+    target_seconds of CPU time, median pass), and on all host cores (dispatch and combine split
+    over token slices, median of 3 passes)."""
+    times, comm = [], 0
+    while sum(times) < target_seconds or len(times) < 3:
+        dt, comm = _oracle_pass(inp)
+        times.append(dt)
+    med = float(np.median(times))
+    nthr = host_threads()
+    par = [_oracle_threaded_pass(inp, nthr) for _ in range(3)]
+    pmed = float(np.median([p[0] for p in par]))
+    model = cpu_model_name()
+    return dict(value=round(comm / 1e9 / med, 3), unit="GB/s", cores=1, kind="oracle", cpu_model=model,
+                sample=f"{len(times)} whole passes (layout + dispatch + combine) of the timed workload, "
+                       f"{sum(times):.1f} s single-threaded, median pass; oracle combine in float64",
+                seconds_per_pass=round(med, 4),
+                all_cores=dict(value=round(par[0][1] / 1e9 / pmed, 3), unit="GB/s", cores=nthr,
+                               seconds_per_pass=round(pmed, 4),
+                               sample=f"median of 3 passes; dispatch and combine of the oracle on {nthr} token "
+                                      f"slices in parallel host threads, layout single-threaded"))
 
 
 def cu_split_streams(n_comm):
@@ -331,6 +431,12 @@ def run_dbo(args):
 
 
 MALL_BYTES = 256 << 20  # MI355X Infinity Cache
+PROBE_LIB_PATH = os.path.join(ROOT, "combine_moe_get_amd", "libmoe_hbm_probe.so")
+# what the path moves and computes in, per quant mode (the JSON line's dtype)
+PAYLOAD = {0: "bf16 dispatch and combine", 1: "int8 dispatch (static), bf16 combine",
+           2: "int8 dispatch + fp32 row scale, bf16 combine"}
+PAYLOAD_DISPATCH = {0: "bf16 rows", 1: "int8 codes (static), fp32 quantization math",
+                    2: "int8 codes + one fp32 scale per row, fp32 quantization math"}
 
 
 def rotation_sets(x_bytes):
@@ -341,27 +447,28 @@ def rotation_sets(x_bytes):
     return int(min(12, max(2, -(-2 * MALL_BYTES // max(int(x_bytes), 1)))))
 
 
-def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False):
+def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False, cid=None, headline=True):
     """One step benchmark of a workload (tokens / ranks override T and P); returns the JSON
-    line without cpu_baseline, and the first input set."""
+    line without cpu_baseline, and the first input set.  headline=False: the workload as named
+    (no --quant / --smooth / --rank-stride overrides) and none of the extra measurements."""
     import torch
 
-    cid = args.workload
+    cid = args.workload if cid is None else cid
     first = workloads.make_inputs(cid, seed=args.seed, T=tokens, P=ranks)
     n_sets = args.rotate if args.rotate else rotation_sets(first["x"].nbytes)
     sets = [first] + [workloads.make_inputs(cid, seed=args.seed + r, T=tokens, P=ranks) for r in range(1, n_sets)]
     c = sets[0]["cfg"]
     T, H, K, E, P, qm = c["T"], c["H"], c["K"], c["E"], c["P"], c["quant_mode"]
-    if args.quant is not None:
+    if args.quant is not None and headline:
         qm = c["quant_mode"] = args.quant
-    if args.smooth is not None:
+    if args.smooth is not None and headline:
         for r, inp in enumerate(sets):
             rng = workloads.rng_for(args.seed + r, cid, 4)
             inp["smooth"] = (None if args.smooth == "none" else
                              rng.uniform(0.5, 1.5, H if args.smooth == "channel" else (E, H)).astype(np.float32))
         c["smooth"] = args.smooth
     shape = mg.make_shape(T, H, K, E, P, c["Z"], c["C"], c["Kc"], c["num_max"])
-    A = mg.rank_capacity(shape) if args.rank_stride == "min" else int(args.rank_stride)
+    A = 0 if not headline else mg.rank_capacity(shape) if args.rank_stride == "min" else int(args.rank_stride)
     cap = P * A if A > 0 else T * K
 
     def d(a):
@@ -508,7 +615,7 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False)
     # the same dispatch kernel writing the same copies in token-major order (row = index of the
     # copy in (token, slot) order): what the expert-major placement the layout prescribes costs
     row_probe = None
-    if args.row_probe:
+    if args.row_probe and headline:
         for g in gsets:
             valid = g["lay"].dst_row >= 0
             tm = torch.cumsum(valid.flatten().to(torch.int32), 0, dtype=torch.int32).view_as(valid) - 1
@@ -520,9 +627,36 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False)
                          what="dispatch kernel, same copies and bytes, rows in expert-major (the layout's) "
                               "or token-major order")
 
+    # the dispatch's write pattern alone: the same row map and bytes, stores only, next to the same
+    # bytes stored in address order (libmoe_hbm_probe.so)
+    write_probe = None
+    if headline and tokens is None and ranks is None and not args.no_write_probe and os.path.exists(PROBE_LIB_PATH):
+        plib = ctypes.CDLL(PROBE_LIB_PATH)
+        plib.moe_probe_scatter_write.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        plib.moe_probe_ordered_write.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        rowb = H * (2 if qm == 0 else 1)
+
+        def probe_call(rc):
+            if rc != 0:
+                raise RuntimeError(f"write-pattern probe refused its arguments ({rc})")
+
+        st_ptr = ctypes.c_void_p(stream.cuda_stream)
+        k_sc = kernel_avg_ms(lambda g: probe_call(plib.moe_probe_scatter_write(
+            ctypes.c_void_p(g["lay"].dst_row.data_ptr()), T, K, rowb, ctypes.c_void_p(g["ex"].data_ptr()), st_ptr)))
+        k_or = kernel_avg_ms(lambda g: probe_call(plib.moe_probe_ordered_write(
+            g["n"], rowb, ctypes.c_void_p(g["ex"].data_ptr()), st_ptr)))
+        wbytes = float(np.mean([g["n"] for g in gsets])) * rowb
+        write_probe = dict(
+            row_bytes=rowb, bytes_per_launch=int(wbytes),
+            scattered_rows_us=round(k_sc * 1e3, 2), scattered_rows_GBps=round(wbytes / 1e9 / (k_sc * 1e-3), 1),
+            address_order_us=round(k_or * 1e3, 2), address_order_GBps=round(wbytes / 1e9 / (k_or * 1e-3), 1),
+            what="stores only (no reads): every receive row of the dispatch's own row map, one workgroup per "
+                 "token as the int8 dispatch, against the same bytes stored in address order")
+
     # the step with layout + dispatch through moe_layout_dispatch (one kernel for T * K <= 8192)
     fused = None
-    if graphs is None:
+    if graphs is None and headline:
         def step_fused(g):
             g["c_ld"](stream)
             g["c_com"](stream)
@@ -564,6 +698,9 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False)
 
     kern = {"dispatch": kstats(k_dis, dis_ms, cb_d, hb_d), "combine": kstats(k_com, com_ms, cb_c, hb_c),
             "layout": kstats(k_lay, lay_ms, None, None)}
+    kern["dispatch"]["payload"] = PAYLOAD_DISPATCH[qm]
+    kern["combine"]["payload"] = "bf16 expert rows in, bf16 out, fp32 accumulation"
+    kern["layout"]["payload"] = "int32 ids and indices"
     kern["layout"]["launches"] = mg.layout_launches(shape)
     dom = "combine" if k_com >= k_dis else "dispatch"
     ach = kern[dom]["hbm_GBps"]
@@ -592,7 +729,7 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False)
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": PAYLOAD[qm] + "; fp32 math",
         "data": "synthetic (seeded generators; no dataset or weights)",
         "config": {"workload": c["name"] + ("" if tokens is None and ranks is None else
                                             f" (T={T}, P={P} override)"), "desc": c["desc"], "T": T, "H": H, "k": K, "E": E, "P": P,
@@ -614,6 +751,8 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False)
         line["fused_layout_dispatch"] = fused
     if row_probe is not None:
         line["row_placement_probe"] = row_probe
+    if write_probe is not None:
+        line["write_pattern_probe"] = write_probe
     return line, sets[0]
 
 
@@ -654,6 +793,11 @@ def main():
                     help="also time the dispatch kernel with token-major receive rows (write-pattern probe)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run a plain 512 MiB device copy 3x (counter calibration)")
+    ap.add_argument("--no-write-probe", action="store_true",
+                    help="skip the write-pattern probe (the dispatch's row map, stores only, vs address order)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other named workloads (each timed like the headline one, summarized in "
+                         "the line's 'workloads' key)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -689,6 +833,34 @@ def main():
             in_step_us_median={k: v["in_step_us_median"] for k, v in sh["kernels"].items()},
             layout_launches=sh["kernels"]["layout"]["launches"],
             fused_layout_dispatch=sh.get("fused_layout_dispatch"))
+    overrides = (args.tokens, args.ranks, args.quant, args.smooth) != (None, None, None, None) or \
+        args.rank_stride not in ("0", 0) or args.graph
+    if not args.no_workloads and not overrides:
+        # every other named workload, timed the same way (layout / dispatch / combine kernels back
+        # to back over rotating input sets), summarized next to the headline one
+        wl = {}
+        for cid in (1, 2, 3, 4, 5):
+            if cid == args.workload:
+                continue
+            sub, _ = measure(args, mg, workloads, dev, cid=cid, headline=False)
+            k = sub["kernels"]
+            cfg = sub["config"]
+            wl[cfg["workload"]] = dict(
+                T=cfg["T"], H=cfg["H"], k=cfg["k"], E=cfg["E"], P=cfg["P"], zero_copy_const=cfg["zero_copy_const"],
+                quant_mode=cfg["quant_mode"], rows_N=cfg["rows_N"], rotating_input_sets=cfg["rotating_input_sets"],
+                us_per_layer=sub["us_per_layer"], value_GBps=sub["value"], pct_of_peak=sub["pct_of_peak"],
+                layout_us=k["layout"]["kernel_us"], layout_launches=k["layout"]["launches"],
+                dispatch=dict((f, k["dispatch"][f]) for f in ("kernel_us", "comm_bytes", "hbm_bytes", "comm_GBps",
+                                                                "comm_pct_of_peak", "hbm_pct_of_peak", "payload")),
+                combine=dict((f, k["combine"][f]) for f in ("kernel_us", "comm_bytes", "hbm_bytes", "comm_GBps",
+                                                              "comm_pct_of_peak", "hbm_pct_of_peak")),
+                device_status=sub["device_status"])
+            print(json.dumps({"workload": cfg["workload"], "us_per_layer": sub["us_per_layer"],
+                              "dispatch_us": k["dispatch"]["kernel_us"], "combine_us": k["combine"]["kernel_us"]}),
+                  file=sys.stderr, flush=True)
+            del sub
+            torch.cuda.empty_cache()
+        line["workloads"] = wl
     if not args.no_probe:
         line["hbm_probe"] = hbm_probe(dev)
     if not args.no_cpu_baseline:

@@ -12,6 +12,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = ["api.hip", "layout.hip", "dispatch.hip", "combine.hip"]
 LIB = os.path.join(HERE, "libmoe_get.so")
+# write-pattern probes the benchmark times next to the dispatch (not part of libmoe_get)
+PROBE_SOURCES = ["hbm_probe.hip"]
+PROBE_LIB = os.path.join(HERE, "libmoe_hbm_probe.so")
 ARCH = "gfx950"
 
 
@@ -32,13 +35,18 @@ def flags():
     ]
 
 
-def build(verbose=False, extra=()):
-    srcs = [os.path.join(HERE, "csrc", s) for s in SOURCES]
-    cmd = [hipcc()] + flags() + list(extra) + ["-o", LIB + ".tmp"] + srcs
+def _compile(sources, lib, verbose, extra):
+    srcs = [os.path.join(HERE, "csrc", s) for s in sources]
+    cmd = [hipcc()] + flags() + list(extra) + ["-o", lib + ".tmp"] + srcs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(lib + ".tmp", lib)
+
+
+def build(verbose=False, extra=()):
+    _compile(SOURCES, LIB, verbose, extra)
+    _compile(PROBE_SOURCES, PROBE_LIB, verbose, extra)
     return LIB
 
 

@@ -33,3 +33,28 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_threaded_oracle_leg_computes_what_the_oracle_computes():
+    # the all-cores CPU baseline runs the oracle's dispatch and combine on token slices in threads;
+    # its rows, scales and combine must be the single-threaded oracle's, bit for bit
+    import numpy as np
+
+    import oracle
+    from combine_moe_get_amd import workloads
+
+    for cid, T in ((2, 256), (4, 512), (5, 512)):
+        inp = workloads.make_inputs(cid, seed=1, T=T)
+        c = inp["cfg"]
+        sh = oracle.make_shape(c["T"], c["H"], c["K"], c["E"], c["P"], c["Z"], c["C"], c["Kc"], c["num_max"])
+        lo = oracle.layout(sh, inp["topk_idx"], inp["mask"])
+        d = oracle.dispatch(sh, c["quant_mode"], inp["x"], lo, smooth=inp["smooth"], topk_idx=inp["topk_idx"])
+        y = np.ascontiguousarray(inp["x"][lo["src_info"] // c["K"]])
+        ref = oracle.combine(sh, y, inp["topk_idx"], inp["topk_weights"], lo, inp["mask"], inp["ori_x"],
+                             inp["alpha1"], inp["alpha2"], inp["const_v"])
+        lo2, ex, ds, out = bench._oracle_threaded_pass(inp, 3, return_outputs=True)
+        assert np.array_equal(lo2["dst_row"], lo["dst_row"])
+        assert np.array_equal(ex, d["expand_x"])
+        if c["quant_mode"] == 2:
+            assert np.array_equal(ds.view(np.uint32), d["dynamic_scales"].view(np.uint32))
+        assert np.array_equal(out, ref)
