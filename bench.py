@@ -257,43 +257,19 @@ def cpu_baseline(inp, target_seconds):
                                       f"slices in parallel host threads, layout single-threaded"))
 
 
-def cu_split_streams(n_comm):
-    """Two HIP streams on disjoint CU sets (hipExtStreamCreateWithCUMask): n_comm CUs spread
-    evenly over the device for the data-movement kernels, the rest for the expert GEMMs.
-    Both streams keep the default priority."""
-    import torch
-
-    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
-    step = n_cu / n_comm
-    comm = {int(i * step) for i in range(n_comm)}
-    words = (n_cu + 31) // 32
-    m_comm = (ctypes.c_uint32 * words)()
-    m_comp = (ctypes.c_uint32 * words)()
-    for cu in range(n_cu):
-        tgt = m_comm if cu in comm else m_comp
-        tgt[cu // 32] |= 1 << (cu % 32)
-    hip = ctypes.CDLL("libamdhip64.so")
-    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
-                                                 ctypes.POINTER(ctypes.c_uint32)]
-    out = []
-    for m in (m_comm, m_comp):
-        h = ctypes.c_void_p()
-        err = hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), words, m)
-        if err != 0:
-            raise RuntimeError(f"hipExtStreamCreateWithCUMask failed ({err})")
-        out.append(torch.cuda.ExternalStream(h.value, device=torch.device("cuda:0")))
-    return out
-
-
 def run_dbo(args):
-    """Dual-batch overlap ("Wide-EP / DBO / DeepEP hardware cliff", section 1) DBO: hiding
-    the wire) on one GPU: the batch is split into two microbatches; each runs layout +
-    dispatch, a stand-in expert computation, and combine.  Sequential: everything on one
-    stream.  Overlapped: layout/dispatch/combine of one microbatch on a second stream while
-    the other microbatch's expert GEMMs run, so t_seq ~ t_comm + t_compute should move toward
-    max(t_comm, t_compute).  The expert stand-in is one dense bf16 GEMM pair per microbatch,
-    rows [N_mb, H] x [H, F] -> relu -> [F, H] (hipBLASLt through torch.matmul), with the
-    same FLOPs as equal-sized experts of intermediate size F."""
+    """Dual-batch overlap ("Wide-EP / DBO / DeepEP hardware cliff", section 1) DBO: hiding the
+    wire) on one GPU: the batch is split into two microbatches; each runs layout + dispatch, a
+    stand-in expert computation, and combine.  Sequential: everything on one stream.  Overlapped:
+    layout/dispatch/combine of the microbatches on a data-movement stream while the other
+    microbatch's expert GEMMs run on a compute stream, so t_seq ~ t_comm + t_compute should move
+    toward max(t_comm, t_compute).  The page's resource split (VLLM_DBO_COMM_SMS compute units
+    for the communication kernels) becomes a cap on the data-movement kernels' grids
+    (moe_dispatch_capped / moe_combine_capped with max_workgroups; 0 = uncapped): they then hold a
+    bounded number of wave slots and walk their work items, leaving the rest to the GEMMs.  The
+    expert stand-in is one dense bf16 GEMM pair per microbatch, rows [N_mb, H] x [H, F] -> relu ->
+    [F, H] (hipBLASLt through torch.matmul), the FLOPs of equal-sized experts of intermediate size
+    F.  Both streams keep the default priority."""
     import torch
 
     import combine_moe_get_amd as mg
@@ -309,34 +285,38 @@ def run_dbo(args):
     shape = mg.make_shape(Tm, H, K, E, P, c["Z"], c["C"], c["Kc"], 0)
 
     def d(a):
+        if a is None:
+            return None
         a = np.ascontiguousarray(a)
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
     gen = torch.Generator(device=dev).manual_seed(args.seed)
+    caps = [int(v) for v in args.dbo_caps.split(",")]
     results = []
-    # one stream pair per CU split, created once (each CU-masked stream holds a hardware
-    # queue of its own; the process needs GPU_MAX_HW_QUEUES above HIP's default of 4)
-    pairs = {}
-    for n_comm in [int(v) for v in args.dbo_comm_cus.split(",")]:
-        pairs[n_comm] = ((torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)) if n_comm == 0
-                         else cu_split_streams(n_comm))
+    s_comm, s_comp = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
     for F in [int(f) for f in args.dbo_f.split(",")]:
         w1 = (torch.randn((H, F), device=dev, generator=gen) / H ** 0.5).to(torch.bfloat16).contiguous()
         w2 = (torch.randn((F, H), device=dev, generator=gen) / F ** 0.5).to(torch.bfloat16).contiguous()
         mbs = []
         for m in range(2):
             sl = slice(m * Tm, (m + 1) * Tm)
-            g = dict(topk=d(inp["topk_idx"][sl]), w=d(inp["topk_weights"][sl]), x=d(inp["x"][sl]))
+            g = dict(topk=d(inp["topk_idx"][sl]), w=d(inp["topk_weights"][sl]), x=d(inp["x"][sl]),
+                     mask=None if inp["mask"] is None else d(inp["mask"][sl]),
+                     ori=None if inp["ori_x"] is None else d(inp["ori_x"][sl]))
             g["lay"] = mg.alloc_layout(shape, dev)
             g["ws"] = mg.alloc_workspace(shape, dev)
-            g["ex"] = torch.empty((Tm * K, H), dtype=torch.bfloat16, device=dev)
+            g["ex"] = torch.zeros((Tm * K, H), dtype=torch.bfloat16, device=dev)
             g["y"] = torch.zeros((Tm * K, H), dtype=torch.bfloat16, device=dev)
             g["out"] = torch.empty((Tm, H), dtype=torch.bfloat16, device=dev)
-            g["c_lay"] = mg.prepare_layout(shape, g["topk"], None, out=g["lay"], workspace=g["ws"])
-            g["c_dis"] = mg.prepare_dispatch(shape, 0, g["x"], g["lay"].dst_row, expand_x=g["ex"])
-            g["c_com"] = mg.prepare_combine(shape, g["y"], g["topk"], g["w"], g["lay"].dst_row, out=g["out"])
+            g["c_lay"] = mg.prepare_layout(shape, g["topk"], g["mask"], out=g["lay"], workspace=g["ws"])
+            for cap in caps:
+                g[("dis", cap)] = mg.prepare_dispatch(shape, 0, g["x"], g["lay"].dst_row, expand_x=g["ex"],
+                                                      max_workgroups=cap)
+                g[("com", cap)] = mg.prepare_combine(shape, g["y"], g["topk"], g["w"], g["lay"].dst_row, g["mask"],
+                                                     g["ori"], d(inp["alpha1"]), d(inp["alpha2"]),
+                                                     d(inp["const_v"]), out=g["out"], max_workgroups=cap)
             mbs.append(g)
 
         def experts(g, st):
@@ -351,18 +331,18 @@ def run_dbo(args):
         def sequential():
             for g in mbs:
                 g["c_lay"](s_main)
-                g["c_dis"](s_main)
+                g[("dis", 0)](s_main)
                 experts(g, s_main)
-                g["c_com"](s_main)
+                g[("com", 0)](s_main)
 
-        def overlapped(s_comm, s_comp):
-            # comm stream: layout+dispatch of both microbatches, then the combines, each
-            # combine after its microbatch's experts; compute stream: the experts
+        def overlapped(cap):
+            # data-movement stream: layout + dispatch of both microbatches, then each combine once
+            # its microbatch's experts are done; compute stream: the experts
             s_comm.wait_stream(s_main)
             s_comp.wait_stream(s_main)
             for m, g in enumerate(mbs):
                 g["c_lay"](s_comm)
-                g["c_dis"](s_comm)
+                g[("dis", cap)](s_comm)
                 ev[m].record(s_comm)
             for m, g in enumerate(mbs):
                 s_comp.wait_event(ev[m])
@@ -370,15 +350,15 @@ def run_dbo(args):
                 ev[2 + m].record(s_comp)
             for m, g in enumerate(mbs):
                 s_comm.wait_event(ev[2 + m])
-                g["c_com"](s_comm)
+                g[("com", cap)](s_comm)
             s_main.wait_stream(s_comm)
             s_main.wait_stream(s_comp)
 
-        def comm_only():
+        def comm_only(cap):
             for g in mbs:
                 g["c_lay"](s_main)
-                g["c_dis"](s_main)
-                g["c_com"](s_main)
+                g[("dis", cap)](s_main)
+                g[("com", cap)](s_main)
 
         def compute_only():
             for g in mbs:
@@ -399,23 +379,15 @@ def run_dbo(args):
         sequential()
         torch.cuda.synchronize()
         ref = [g["out"].clone() for g in mbs]
-        t_comm, t_comp = timed(comm_only), timed(compute_only)
+        t_comm, t_comp = timed(lambda: comm_only(0)), timed(compute_only)
         t_seq = timed(sequential)
         flops = 2 * 2 * (Tm * K) * H * F * 2  # two microbatches, two GEMMs each
-        for n_comm, (s_comm, s_comp) in pairs.items():  # n_comm 0: two streams sharing every CU
-            t_dbo = timed(lambda: overlapped(s_comm, s_comp))
-            # the comm kernels alone on their share of the CUs
-            def comm_masked():
-                s_comm.wait_stream(s_main)
-                for g in mbs:
-                    g["c_lay"](s_comm)
-                    g["c_dis"](s_comm)
-                    g["c_com"](s_comm)
-                s_main.wait_stream(s_comm)
-            t_comm_share = timed(comm_masked)
+        for cap in caps:
+            t_dbo = timed(lambda: overlapped(cap))
+            t_comm_cap = timed(lambda: comm_only(cap))
             same = all(torch.equal(g["out"], r) for g, r in zip(mbs, ref))
-            results.append(dict(F=F, comm_cus=n_comm if n_comm else "all (unmasked)",
-                                t_comm_us=round(t_comm, 1), t_comm_on_share_us=round(t_comm_share, 1),
+            results.append(dict(F=F, comm_max_workgroups=cap if cap else "uncapped",
+                                t_comm_us=round(t_comm, 1), t_comm_capped_us=round(t_comm_cap, 1),
                                 t_compute_us=round(t_comp, 1), t_seq_us=round(t_seq, 1),
                                 t_dbo_us=round(t_dbo, 1), ideal_us=round(max(t_comm, t_comp), 1),
                                 saved_frac_of_comm=round((t_seq - t_dbo) / max(t_comm, 1e-9), 3),
@@ -783,8 +755,8 @@ def main():
     ap.add_argument("--dbo", action="store_true",
                     help="dual-batch overlap measurement instead of the step benchmark (prints its own JSON line)")
     ap.add_argument("--dbo-f", default="256,512,2048", help="expert intermediate sizes F for --dbo")
-    ap.add_argument("--dbo-comm-cus", default="0",
-                    help="CUs given to the data-movement stream in --dbo (0: no split; a split needs CU-masked streams)")
+    ap.add_argument("--dbo-caps", default="0,512,1024,2048,4096",
+                    help="grid caps (max workgroups) of the data-movement kernels in --dbo; 0 = uncapped")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the HBM probe (fill and copy of a 2 GiB buffer with library kernels)")
     ap.add_argument("--no-share", action="store_true",

@@ -114,8 +114,12 @@ def lib():
         L.moe_layout_dispatch_launches.restype = ctypes.c_int
         L.moe_dispatch.argtypes = [SP, I32, V, V, I32, V, V, V, V, V, V, V]
         L.moe_dispatch.restype = ctypes.c_int
+        L.moe_dispatch_capped.argtypes = [SP, I32, I32, V, V, I32, V, V, V, V, V, V, V]
+        L.moe_dispatch_capped.restype = ctypes.c_int
         L.moe_combine.argtypes = [SP] + [V] * 11
         L.moe_combine.restype = ctypes.c_int
+        L.moe_combine_capped.argtypes = [SP, I32] + [V] * 11
+        L.moe_combine_capped.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -301,8 +305,9 @@ def layout(shape, topk_idx, x_active_mask=None, out=None, workspace=None, stream
 
 
 def prepare_dispatch(shape, quant_mode, x, dst_row, x_smooth_scale=None, topk_weights=None, topk_idx=None,
-                     expand_x=None, dynamic_scales=None, expand_weights=None, rows=None):
-    """Checked, marshalled moe_dispatch call; see dispatch()."""
+                     expand_x=None, dynamic_scales=None, expand_weights=None, rows=None, max_workgroups=0):
+    """Checked, marshalled moe_dispatch call (moe_dispatch_capped when max_workgroups > 0); see
+    dispatch()."""
     T, H, K, E = shape.num_tokens, shape.hidden, shape.topk, shape.num_experts
     if x is None or dst_row is None:
         raise ValueError("x and dst_row are required")
@@ -331,23 +336,27 @@ def prepare_dispatch(shape, quant_mode, x, dst_row, x_smooth_scale=None, topk_we
         None,
     ]
     keep = (shape, x, dst_row, x_smooth_scale, topk_weights, topk_idx)
+    if int(max_workgroups) != 0:  # negative: the library refuses it
+        return PreparedCall(lib().moe_dispatch_capped, args[:1] + [int(max_workgroups)] + args[1:],
+                            "moe_dispatch_capped", keep, (expand_x, dynamic_scales, expand_weights))
     return PreparedCall(lib().moe_dispatch, args, "moe_dispatch", keep,
                         (expand_x, dynamic_scales, expand_weights))
 
 
 def dispatch(shape, quant_mode, x, dst_row, x_smooth_scale=None, topk_weights=None, topk_idx=None,
-             expand_x=None, dynamic_scales=None, expand_weights=None, stream=None, rows=None):
+             expand_x=None, dynamic_scales=None, expand_weights=None, stream=None, rows=None, max_workgroups=0):
     """moe_dispatch.  Returns (expand_x [rows, H], dynamic_scales [rows] or None,
     expand_weights [rows] or None); rows not named by dst_row are left as they were.
     `rows` (default T * K) sizes the outputs allocated here; a fixed-capacity layout
-    needs P * rank_stride."""
+    needs P * rank_stride.  max_workgroups > 0 caps the grid (moe_dispatch_capped)."""
     return prepare_dispatch(shape, quant_mode, x, dst_row, x_smooth_scale, topk_weights, topk_idx,
-                            expand_x, dynamic_scales, expand_weights, rows)(stream)
+                            expand_x, dynamic_scales, expand_weights, rows, max_workgroups)(stream)
 
 
 def prepare_combine(shape, expert_out, topk_idx, topk_weights, dst_row, x_active_mask=None, ori_x=None,
-                    const_alpha1=None, const_alpha2=None, const_v=None, out=None, rows=None):
-    """Checked, marshalled moe_combine call; see combine()."""
+                    const_alpha1=None, const_alpha2=None, const_v=None, out=None, rows=None, max_workgroups=0):
+    """Checked, marshalled moe_combine call (moe_combine_capped when max_workgroups > 0); see
+    combine()."""
     T, H, K = shape.num_tokens, shape.hidden, shape.topk
     special = shape.copy_expert_num + shape.const_expert_num > 0
     kc = shape.const_expert_num
@@ -370,16 +379,21 @@ def prepare_combine(shape, expert_out, topk_idx, topk_weights, dst_row, x_active
     ]
     keep = (shape, expert_out, topk_idx, topk_weights, dst_row, x_active_mask, ori_x, const_alpha1,
             const_alpha2, const_v)
+    if int(max_workgroups) != 0:  # negative: the library refuses it
+        return PreparedCall(lib().moe_combine_capped, args[:1] + [int(max_workgroups)] + args[1:],
+                            "moe_combine_capped", keep, out)
     return PreparedCall(lib().moe_combine, args, "moe_combine", keep, out)
 
 
 def combine(shape, expert_out, topk_idx, topk_weights, dst_row, x_active_mask=None, ori_x=None,
-            const_alpha1=None, const_alpha2=None, const_v=None, out=None, stream=None, rows=None):
+            const_alpha1=None, const_alpha2=None, const_v=None, out=None, stream=None, rows=None,
+            max_workgroups=0):
     """moe_combine.  Returns out [T, H] bf16.  `rows` is the number of receive rows expert_out
     must hold (default T * K, which covers every compact layout; a fixed-capacity layout needs
-    P * rank_stride; a caller that knows N may pass rows=N)."""
+    P * rank_stride; a caller that knows N may pass rows=N).  max_workgroups > 0 caps the grid
+    (moe_combine_capped)."""
     return prepare_combine(shape, expert_out, topk_idx, topk_weights, dst_row, x_active_mask, ori_x,
-                           const_alpha1, const_alpha2, const_v, out, rows)(stream)
+                           const_alpha1, const_alpha2, const_v, out, rows, max_workgroups)(stream)
 
 
 def _smooth_rows(shape, x_smooth_scale):

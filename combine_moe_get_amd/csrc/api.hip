@@ -324,14 +324,23 @@ int moe_dispatch(const moe_get_shape_t *shape, int32_t quant_mode, const uint16_
                  const float *x_smooth_scale, int32_t smooth_rows, const float *topk_weights,
                  const int32_t *topk_idx, const int32_t *dst_row, void *expand_x,
                  float *dynamic_scales, float *expand_weights, void *stream) {
+  return moe_dispatch_capped(shape, 0, quant_mode, x, x_smooth_scale, smooth_rows, topk_weights, topk_idx, dst_row,
+                             expand_x, dynamic_scales, expand_weights, stream);
+}
+
+int moe_dispatch_capped(const moe_get_shape_t *shape, int32_t max_workgroups, int32_t quant_mode, const uint16_t *x,
+                        const float *x_smooth_scale, int32_t smooth_rows, const float *topk_weights,
+                        const int32_t *topk_idx, const int32_t *dst_row, void *expand_x, float *dynamic_scales,
+                        float *expand_weights, void *stream) {
+  if (max_workgroups < 0) return MOE_ERR_ARG;
   DispatchArgs a;
   bool per_expert = false;
   const int st = dispatch_args(shape, quant_mode, x, x_smooth_scale, smooth_rows, topk_weights, topk_idx, dst_row,
                                expand_x, dynamic_scales, expand_weights, a, per_expert);
   if (st != MOE_OK) return st;
   if (a.T == 0) return MOE_OK;
-  return launch_dispatch(a, quant_mode, per_expert, (hipStream_t)stream) == hipSuccess ? MOE_OK
-                                                                                      : MOE_ERR_HIP;
+  return launch_dispatch(a, quant_mode, per_expert, (hipStream_t)stream, max_workgroups) == hipSuccess ? MOE_OK
+                                                                                                      : MOE_ERR_HIP;
 }
 
 int moe_layout_dispatch(const moe_get_shape_t *shape, int64_t rank_stride, int32_t quant_mode,
@@ -367,6 +376,15 @@ int moe_combine(const moe_get_shape_t *shape, const uint16_t *expert_out,
                 const uint8_t *x_active_mask, const int32_t *dst_row, const uint16_t *ori_x,
                 const uint16_t *const_alpha1, const uint16_t *const_alpha2,
                 const uint16_t *const_v, uint16_t *out, void *stream) {
+  return moe_combine_capped(shape, 0, expert_out, topk_idx, topk_weights, x_active_mask, dst_row, ori_x,
+                            const_alpha1, const_alpha2, const_v, out, stream);
+}
+
+int moe_combine_capped(const moe_get_shape_t *shape, int32_t max_workgroups, const uint16_t *expert_out,
+                       const int32_t *topk_idx, const float *topk_weights, const uint8_t *x_active_mask,
+                       const int32_t *dst_row, const uint16_t *ori_x, const uint16_t *const_alpha1,
+                       const uint16_t *const_alpha2, const uint16_t *const_v, uint16_t *out, void *stream) {
+  if (max_workgroups < 0) return MOE_ERR_ARG;
   const int st = check_shape(shape);
   if (st != MOE_OK) return st;
   const int T = shape->num_tokens;
@@ -397,7 +415,7 @@ int moe_combine(const moe_get_shape_t *shape, const uint16_t *expert_out,
   a.Z = shape->zero_expert_num;
   a.C = C;
   a.Kc = Kc;
-  return launch_combine(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  return launch_combine(a, (hipStream_t)stream, max_workgroups) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 }  // extern "C"

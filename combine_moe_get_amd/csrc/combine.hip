@@ -45,10 +45,9 @@ __device__ __forceinline__ float bf16_at(const u32x4 &v, int e) {
 // One wave per workgroup: measured on gfx950 at T=4096, H=7168, top-8 with every input read from
 // HBM, 89.5 us against 91 us for four waves per workgroup (and 91 / 91 us for two / eight).
 template <int KMAX, bool SPECIAL>
-__global__ void __launch_bounds__(64) combine_kernel(CombineArgs a, int nslice) {
+__device__ __forceinline__ void combine_item(const CombineArgs &a, int nslice, int gw) {
   constexpr int U = 2;
   const int lane = threadIdx.x;
-  const int gw = blockIdx.x;
   const int t = gw / nslice, sl = gw - t * nslice;
   if (t >= a.T) return;  // whole wave
   const int H = a.H, K = a.K;
@@ -146,6 +145,18 @@ __global__ void __launch_bounds__(64) combine_kernel(CombineArgs a, int nslice) 
   }
 }
 
+// items: T * nslice (token, slice) pairs.  LOOP: a capped grid walks them with a grid stride;
+// otherwise one workgroup per item (the loop costs registers: 76 -> 82 at top-8, one wave per
+// SIMD less)
+template <int KMAX, bool SPECIAL, bool LOOP>
+__global__ void __launch_bounds__(64) combine_kernel(CombineArgs a, int nslice, int items) {
+  if constexpr (LOOP) {
+    for (int gw = blockIdx.x; gw < items; gw += gridDim.x) combine_item<KMAX, SPECIAL>(a, nslice, gw);
+  } else {
+    combine_item<KMAX, SPECIAL>(a, nslice, blockIdx.x);
+  }
+}
+
 // Routed slots only, rows of NS 2 KB slices: one wave per whole token, its output row kept in
 // registers and written after all of the token's reads.  The waves resident together then read
 // first and write together, instead of every wave writing 2 KB between other waves' reads.
@@ -157,9 +168,8 @@ __global__ void __launch_bounds__(64) combine_kernel(CombineArgs a, int nslice) 
 // Arithmetic per element is the slice kernel's (same slot order, same fma chain), so the
 // results are bit-identical.
 template <int KMAX, int NS>
-__global__ void __launch_bounds__(64) combine_row_kernel(CombineArgs a) {
+__device__ __forceinline__ void combine_row_item(const CombineArgs &a, int t) {
   const int lane = threadIdx.x;
-  const int t = blockIdx.x;
   if (t >= a.T) return;  // whole wave
   const int H = a.H, K = a.K;
   const int nch = H >> 3;
@@ -215,27 +225,43 @@ __global__ void __launch_bounds__(64) combine_row_kernel(CombineArgs a) {
   }
 }
 
+// one wave per token (uncapped launches only)
+template <int KMAX, int NS>
+__global__ void __launch_bounds__(64) combine_row_kernel(CombineArgs a) {
+  combine_row_item<KMAX, NS>(a, blockIdx.x);
+}
+
 template <int KMAX>
-static void launch_k(const CombineArgs &a, hipStream_t st) {
+static void launch_k(const CombineArgs &a, hipStream_t st, int max_wg) {
   const int nch = a.H / 8;
   const int nslice = (nch + 127) / 128;
-  const int64_t waves = (int64_t)a.T * nslice;
-  const dim3 g((unsigned)waves);
+  const int64_t items = (int64_t)a.T * nslice;
+  if (max_wg > 0) {  // capped grid: the slice kernel walking its items
+    const dim3 g((unsigned)(items > max_wg ? max_wg : items));
+    if (a.C + a.Kc > 0)
+      hipLaunchKernelGGL((combine_kernel<KMAX, true, true>), g, dim3(64), 0, st, a, nslice, (int)items);
+    else
+      hipLaunchKernelGGL((combine_kernel<KMAX, false, true>), g, dim3(64), 0, st, a, nslice, (int)items);
+    return;
+  }
+  const dim3 g((unsigned)items);
   if (a.C + a.Kc > 0)
-    hipLaunchKernelGGL((combine_kernel<KMAX, true>), g, dim3(64), 0, st, a, nslice);
+    hipLaunchKernelGGL((combine_kernel<KMAX, true, false>), g, dim3(64), 0, st, a, nslice, (int)items);
   else if (KMAX == 8 && nslice == 7 && a.T >= 2048 && !a.mask)  // see combine_row_kernel
     hipLaunchKernelGGL((combine_row_kernel<8, 7>), dim3((unsigned)a.T), dim3(64), 0, st, a);
   else  // no copy / constant ids can occur: the routed-only kernel needs fewer registers
-    hipLaunchKernelGGL((combine_kernel<KMAX, false>), g, dim3(64), 0, st, a, nslice);
+    hipLaunchKernelGGL((combine_kernel<KMAX, false, false>), g, dim3(64), 0, st, a, nslice, (int)items);
 }
 
-hipError_t launch_combine(const CombineArgs &a, hipStream_t stream) {
+// max_wg > 0 caps the grid (the kernels then walk their items with a grid stride); a capped
+// launch keeps the slice kernel, whose small waves spread a bounded grid over more of the row
+hipError_t launch_combine(const CombineArgs &a, hipStream_t stream, int max_wg) {
   if (a.T == 0) return hipSuccess;
-  if (a.K <= 1) launch_k<1>(a, stream);
-  else if (a.K <= 2) launch_k<2>(a, stream);
-  else if (a.K <= 4) launch_k<4>(a, stream);
-  else if (a.K <= 8) launch_k<8>(a, stream);
-  else launch_k<16>(a, stream);
+  if (a.K <= 1) launch_k<1>(a, stream, max_wg);
+  else if (a.K <= 2) launch_k<2>(a, stream, max_wg);
+  else if (a.K <= 4) launch_k<4>(a, stream, max_wg);
+  else if (a.K <= 8) launch_k<8>(a, stream, max_wg);
+  else launch_k<16>(a, stream, max_wg);
   return hipGetLastError();
 }
 

@@ -38,9 +38,8 @@ namespace moe {
 // stores then): 104.2-104.6 us against 105.6-106.5 us for 1 KB slices in four-wave workgroups.
 // With buffer-resource loads and sc1 stores (98-100 us), 1, 3 and 4 KB slices measured
 // 102.6-103.5, 104.7-105.3 and 106.2-106.7 us against 100.1-100.8 us for 2 KB in one run.
-__global__ void __launch_bounds__(64) dispatch_copy_kernel(DispatchArgs a, int nslice) {
+__device__ __forceinline__ void dispatch_copy_item(const DispatchArgs &a, int nslice, int gw) {
   const int lane = threadIdx.x;
-  const int gw = blockIdx.x;
   const int t = gw / nslice, sl = gw - t * nslice;
   if (t >= a.T) return;
   const int K = a.K, H = a.H, nch = H >> 3;
@@ -68,17 +67,26 @@ __global__ void __launch_bounds__(64) dispatch_copy_kernel(DispatchArgs a, int n
   if (write_w) a.expand_w[myrow] = a.w ? a.w[(size_t)t * K + lane] : 1.0f;
 }
 
+// items: T * nslice (token, slice) pairs.  LOOP: a grid smaller than that (a capped launch) walks
+// them with a grid stride; otherwise one workgroup per item (the loop costs registers: 12 -> 18)
+template <bool LOOP>
+__global__ void __launch_bounds__(64) dispatch_copy_kernel(DispatchArgs a, int nslice, int items) {
+  if constexpr (LOOP) {
+    for (int gw = blockIdx.x; gw < items; gw += gridDim.x) dispatch_copy_item(a, nslice, gw);
+  } else {
+    dispatch_copy_item(a, nslice, blockIdx.x);
+  }
+}
+
 // ---- int8 (static or dynamic) -----------------------------------------------
 // one workgroup per token, blockDim = 64 * ceil(pairs / 64) <= 512; lane p of the
 // block owns channels [16p, 16p + 16) (chunks 2p and 2p + 1).  One code row per
 // token (no smoothing, or one smooth vector for all experts), stored to every
 // routed copy.
 template <int MODE>
-__global__ void __launch_bounds__(512) dispatch_quant_kernel(DispatchArgs a) {
-  __shared__ float red[8];
+__device__ __forceinline__ void dispatch_quant_item(const DispatchArgs &a, int t, float (*red)[8], int &par) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
-  const int t = blockIdx.x;
   const int K = a.K, H = a.H;
 
   // every load of the lane is issued before the first use: slot rows, row chunks, scales.
@@ -105,9 +113,10 @@ __global__ void __launch_bounds__(512) dispatch_quant_kernel(DispatchArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(g[e]));
     m = wave_max(m);
-    if (lane == 0) red[wv] = m;
+    if (lane == 0) red[par][wv] = m;
     __syncthreads();
-    const float amax = block_max_of(red, nw);
+    const float amax = block_max_of(red[par], nw);
+    par ^= 1;
     dyn = amax > 0.0f ? 127.0f / amax : 0.0f;
     if (wv == 0 && myrow >= 0 && a.dyn_scales) a.dyn_scales[myrow] = amax > 0.0f ? 1.0f / dyn : 0.0f;
   }
@@ -118,6 +127,20 @@ __global__ void __launch_bounds__(512) dispatch_quant_kernel(DispatchArgs a) {
     q.store_codes<MODE>(g, dyn, (int8_t *)a.expand_x + (size_t)readlane(myrow, j) * H);
   }
   if (write_w) a.expand_w[myrow] = a.w ? a.w[(size_t)t * K + lane] : 1.0f;
+}
+
+// items: the T tokens.  With a capped grid a workgroup quantizes several tokens in turn; the two
+// halves of red[][] alternate from one amax to the next (across tokens too), so one barrier per
+// token keeps a wave's next write away from the half the slower waves still read.
+template <int MODE, bool LOOP>
+__global__ void __launch_bounds__(512) dispatch_quant_kernel(DispatchArgs a) {
+  __shared__ float red[2][8];
+  int par = 0;
+  if constexpr (LOOP) {
+    for (int t = blockIdx.x; t < a.T; t += gridDim.x) dispatch_quant_item<MODE>(a, t, red, par);
+  } else {
+    dispatch_quant_item<MODE>(a, blockIdx.x, red, par);
+  }
 }
 
 // ---- int8 with per-expert smooth scales [E, H] --------------------------------
@@ -138,12 +161,12 @@ template <int MODE>
 constexpr int expert_groups() { return MODE == 1 ? 2 : 1; }
 
 template <int MODE>
-__global__ void __launch_bounds__(512) dispatch_quant_expert_kernel(DispatchArgs a) {
+__device__ __forceinline__ void dispatch_quant_expert_item(const DispatchArgs &a, int item, float (*red)[8],
+                                                           int &par) {
   constexpr int G = expert_groups<MODE>();
-  __shared__ float red[2][8];  // alternated per copy: one barrier per copy suffices
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
-  const int t = blockIdx.x / G, grp = blockIdx.x % G;
+  const int t = item / G, grp = item % G;
   const int K = a.K, H = a.H;
 
   int myrow = -1, myid = 0;
@@ -162,7 +185,6 @@ __global__ void __launch_bounds__(512) dispatch_quant_expert_kernel(DispatchArgs
   float f[16];
   unpack8(v0, f);
   unpack8(v1, f + 8);
-  int par = 0;
   while (sel) {
     const int j = __builtin_ctzll(sel);
     sel &= sel - 1;
@@ -188,27 +210,51 @@ __global__ void __launch_bounds__(512) dispatch_quant_expert_kernel(DispatchArgs
   }
 }
 
-hipError_t launch_dispatch(const DispatchArgs &a, int quant_mode, bool per_expert, hipStream_t stream) {
-  if (a.T == 0) return hipSuccess;
+// items: T * G (token, expert-id group) pairs; the halves of red[][] alternate per copy, across
+// items too (see dispatch_quant_kernel)
+template <int MODE, bool LOOP>
+__global__ void __launch_bounds__(512) dispatch_quant_expert_kernel(DispatchArgs a, int items) {
+  __shared__ float red[2][8];
+  int par = 0;
+  if constexpr (LOOP) {
+    for (int it = blockIdx.x; it < items; it += gridDim.x) dispatch_quant_expert_item<MODE>(a, it, red, par);
+  } else {
+    dispatch_quant_expert_item<MODE>(a, blockIdx.x, red, par);
+  }
+}
+
+template <bool LOOP>
+static void launch_dispatch_grid(const DispatchArgs &a, int quant_mode, bool per_expert, hipStream_t stream,
+                                 int max_wg) {
+  // grid over `items` work items: one workgroup per item, or at most max_wg (LOOP)
+  auto grid = [max_wg](int64_t items) { return dim3((unsigned)(LOOP && items > max_wg ? max_wg : items)); };
   const int nch = a.H / 8;
   if (quant_mode == 0) {
     const int nslice = (nch + 127) / 128;
-    const int64_t waves = (int64_t)a.T * nslice;
-    hipLaunchKernelGGL(dispatch_copy_kernel, dim3((unsigned)waves), dim3(64), 0, stream, a, nslice);
-    return hipGetLastError();
+    const int64_t items = (int64_t)a.T * nslice;
+    hipLaunchKernelGGL(dispatch_copy_kernel<LOOP>, grid(items), dim3(64), 0, stream, a, nslice, (int)items);
+    return;
   }
   const int pairs = (nch + 1) / 2;  // <= 512 for H <= 8192
   const dim3 blk(64 * ((pairs + 63) / 64));
-  const dim3 g((unsigned)a.T);
-  const dim3 ge1((unsigned)((int64_t)a.T * expert_groups<1>())), ge2((unsigned)((int64_t)a.T * expert_groups<2>()));
+  const int64_t ie1 = (int64_t)a.T * expert_groups<1>(), ie2 = (int64_t)a.T * expert_groups<2>();
   if (quant_mode == 1 && !per_expert)
-    hipLaunchKernelGGL((dispatch_quant_kernel<1>), g, blk, 0, stream, a);
+    hipLaunchKernelGGL((dispatch_quant_kernel<1, LOOP>), grid(a.T), blk, 0, stream, a);
   else if (quant_mode == 1)
-    hipLaunchKernelGGL((dispatch_quant_expert_kernel<1>), ge1, blk, 0, stream, a);
+    hipLaunchKernelGGL((dispatch_quant_expert_kernel<1, LOOP>), grid(ie1), blk, 0, stream, a, (int)ie1);
   else if (!per_expert)
-    hipLaunchKernelGGL((dispatch_quant_kernel<2>), g, blk, 0, stream, a);
+    hipLaunchKernelGGL((dispatch_quant_kernel<2, LOOP>), grid(a.T), blk, 0, stream, a);
   else
-    hipLaunchKernelGGL((dispatch_quant_expert_kernel<2>), ge2, blk, 0, stream, a);
+    hipLaunchKernelGGL((dispatch_quant_expert_kernel<2, LOOP>), grid(ie2), blk, 0, stream, a, (int)ie2);
+}
+
+hipError_t launch_dispatch(const DispatchArgs &a, int quant_mode, bool per_expert, hipStream_t stream,
+                           int max_wg) {
+  if (a.T == 0) return hipSuccess;
+  if (max_wg > 0)
+    launch_dispatch_grid<true>(a, quant_mode, per_expert, stream, max_wg);
+  else
+    launch_dispatch_grid<false>(a, quant_mode, per_expert, stream, 0);
   return hipGetLastError();
 }
 

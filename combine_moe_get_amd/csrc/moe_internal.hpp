@@ -176,8 +176,11 @@ int layout_launch_count(const LayoutArgs &a);  // kernels launch_layout runs for
 hipError_t launch_layout_dispatch(const LayoutArgs &a, const DispatchArgs &d, int quant_mode, bool per_expert,
                                   hipStream_t stream);
 int layout_dispatch_launch_count(const LayoutArgs &a);
-hipError_t launch_dispatch(const DispatchArgs &a, int quant_mode, bool per_expert, hipStream_t stream);
-hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
+// max_wg > 0: launch at most that many workgroups, each walking several work items (a capped
+// grid, which leaves the rest of the GPU to kernels running beside it); 0: one per item
+hipError_t launch_dispatch(const DispatchArgs &a, int quant_mode, bool per_expert, hipStream_t stream,
+                           int max_wg = 0);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t stream, int max_wg = 0);
 
 // LDS bytes of the layout count kernel and its waves per block
 int layout_waves(int E);

@@ -206,6 +206,17 @@ int moe_dispatch(const moe_get_shape_t *shape, int32_t quant_mode, const uint16_
                  const int32_t *topk_idx, const int32_t *dst_row, void *expand_x,
                  float *dynamic_scales, float *expand_weights, void *stream);
 
+/* moe_dispatch on a capped grid: at most max_workgroups workgroups, each quantizing and
+ * scattering several work items in turn (max_workgroups 0: one per item, exactly moe_dispatch;
+ * negative: MOE_ERR_ARG).  Results are those of moe_dispatch bit for bit.  It bounds the part of
+ * the GPU the data movement holds, so that it can run beside other kernels on other streams --
+ * the compute-unit reservation of dual-batch overlap ("Wide-EP / DBO / DeepEP hardware cliff",
+ * section 1) DBO: hiding the wire, VLLM_DBO_COMM_SMS) -- without masking compute units. */
+int moe_dispatch_capped(const moe_get_shape_t *shape, int32_t max_workgroups, int32_t quant_mode, const uint16_t *x,
+                        const float *x_smooth_scale, int32_t smooth_rows, const float *topk_weights,
+                        const int32_t *topk_idx, const int32_t *dst_row, void *expand_x, float *dynamic_scales,
+                        float *expand_weights, void *stream);
+
 /* Layout and dispatch in one call, the way the CANN dispatch operator returns
  * the routing layout (expert_token_nums, ep_recv_counts, assist_info_for_combine)
  * together with the dispatched rows (its Prototype and Formula).  Results are
@@ -251,6 +262,13 @@ int moe_combine(const moe_get_shape_t *shape, const uint16_t *expert_out,
                 const uint8_t *x_active_mask, const int32_t *dst_row, const uint16_t *ori_x,
                 const uint16_t *const_alpha1, const uint16_t *const_alpha2,
                 const uint16_t *const_v, uint16_t *out, void *stream);
+
+/* moe_combine on a capped grid (see moe_dispatch_capped): at most max_workgroups workgroups,
+ * results identical to moe_combine bit for bit; 0 means uncapped. */
+int moe_combine_capped(const moe_get_shape_t *shape, int32_t max_workgroups, const uint16_t *expert_out,
+                       const int32_t *topk_idx, const float *topk_weights, const uint8_t *x_active_mask,
+                       const int32_t *dst_row, const uint16_t *ori_x, const uint16_t *const_alpha1,
+                       const uint16_t *const_alpha2, const uint16_t *const_v, uint16_t *out, void *stream);
 
 #ifdef __cplusplus
 }
