@@ -601,7 +601,7 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False,
 
     # the dispatch's write pattern alone: the same row map and bytes, stores only, next to the same
     # bytes stored in address order (libmoe_hbm_probe.so)
-    write_probe = None
+    write_probe = read_probe = None
     if headline and tokens is None and ranks is None and not args.no_write_probe and os.path.exists(PROBE_LIB_PATH):
         plib = ctypes.CDLL(PROBE_LIB_PATH)
         plib.moe_probe_scatter_write.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -618,11 +618,27 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False,
             ctypes.c_void_p(g["lay"].dst_row.data_ptr()), T, K, rowb, ctypes.c_void_p(g["ex"].data_ptr()), st_ptr)))
         k_or = kernel_avg_ms(lambda g: probe_call(plib.moe_probe_ordered_write(
             g["n"], rowb, ctypes.c_void_p(g["ex"].data_ptr()), st_ptr)))
+        # the combine's reads alone: its rows gathered in its launch shape, no output rows written
+        plib.moe_probe_gather_read.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        nsl = (2 * H // 16 + 127) // 128
+        sink = torch.empty((T * nsl * 64, 4), dtype=torch.int32, device=dev)
+        k_rd = kernel_avg_ms(lambda g: probe_call(plib.moe_probe_gather_read(
+            ctypes.c_void_p(g["lay"].dst_row.data_ptr()), T, K, 2 * H, ctypes.c_void_p(g["y"].data_ptr()),
+            ctypes.c_void_p(sink.data_ptr()), st_ptr)))
+        rbytes = float(np.mean([g["n"] for g in gsets])) * 2 * H
+        read_probe = dict(row_bytes=2 * H, bytes_per_launch=int(rbytes), gathered_rows_us=round(k_rd * 1e3, 2),
+                          gathered_rows_GBps=round(rbytes / 1e9 / (k_rd * 1e-3), 1),
+                          combine_kernel_us=round(k_com * 1e3, 2),
+                          what="reads only: the combine's expert-output rows gathered in its launch shape (one wave "
+                               "per token and 2 KB slice, non-temporal loads), no output rows written")
+        del sink
         wbytes = float(np.mean([g["n"] for g in gsets])) * rowb
         write_probe = dict(
             row_bytes=rowb, bytes_per_launch=int(wbytes),
             scattered_rows_us=round(k_sc * 1e3, 2), scattered_rows_GBps=round(wbytes / 1e9 / (k_sc * 1e-3), 1),
             address_order_us=round(k_or * 1e3, 2), address_order_GBps=round(wbytes / 1e9 / (k_or * 1e-3), 1),
+            dispatch_kernel_us=round(k_dis * 1e3, 2),
             what="stores only (no reads): every receive row of the dispatch's own row map, one workgroup per "
                  "token as the int8 dispatch, against the same bytes stored in address order")
 
@@ -725,6 +741,8 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False,
         line["row_placement_probe"] = row_probe
     if write_probe is not None:
         line["write_pattern_probe"] = write_probe
+    if read_probe is not None:
+        line["read_pattern_probe"] = read_probe
     return line, sets[0]
 
 
@@ -766,7 +784,8 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run a plain 512 MiB device copy 3x (counter calibration)")
     ap.add_argument("--no-write-probe", action="store_true",
-                    help="skip the write-pattern probe (the dispatch's row map, stores only, vs address order)")
+                    help="skip the access-pattern probes (the dispatch's row map, stores only, vs address order; "
+                         "the combine's rows, reads only)")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the other named workloads (each timed like the headline one, summarized in "
                          "the line's 'workloads' key)")

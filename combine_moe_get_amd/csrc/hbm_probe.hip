@@ -1,5 +1,5 @@
-// hbm_probe.hip -- write-pattern probes for the roofline of the dispatch (libmoe_hbm_probe.so,
-// loaded by the benchmark only; the dispatch / combine library does not use it).
+// hbm_probe.hip -- access-pattern probes for the rooflines of the dispatch and the combine
+// (libmoe_hbm_probe.so, loaded by the benchmark only; the dispatch / combine library does not use it).
 //
 // The dispatch writes every routed copy of a token into a receive row somewhere in an
 // expert-major buffer: rows land at scattered places.  These kernels store the same bytes with
@@ -7,7 +7,8 @@
 // of the int8 dispatch (one workgroup per token, one lane per 16 bytes of the row, every copy
 // stored by all lanes), and (b) in address order (one workgroup per run of 8 consecutive rows),
 // so the benchmark can report what HBM accepts for each pattern next to the dispatch itself.
-// Stores are non-temporal, as the int8 dispatch's.
+// Stores are non-temporal, as the int8 dispatch's.  The gather probe is the combine's read side
+// alone: the same rows read in the combine's launch shape, with no output rows written.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,6 +41,39 @@ __global__ void __launch_bounds__(1024) probe_ordered_kernel(int64_t nrows, int 
   }
 }
 
+// reads only: one wave per (token, 2 KB slice of the row), as the combine's slice kernel -- lane l
+// loads the 16-byte chunks l and l + 64 of the slice from each of the token's K rows named by
+// dst_row (non-temporal loads, all issued before any use) and folds them with XOR; a lane stores
+// its 16-byte fold to `sink` only if it equals one fixed 128-bit pattern (never, in practice), so
+// the loads cannot be dropped while the stores add no traffic
+template <int KMAX>
+__global__ void __launch_bounds__(64) probe_gather_kernel(const int32_t *dst_row, int K, int row_bytes,
+                                                          const unsigned char *buf, int nslice, u32x4 *sink) {
+  const int lane = threadIdx.x;
+  const int gw = blockIdx.x;
+  const int t = gw / nslice, sl = gw - t * nslice;
+  const int nch = row_bytes / 16;
+  const int c0 = 128 * sl + lane, c1 = c0 + 64;
+  int myrow = -1;
+  if (lane < K) myrow = dst_row[(size_t)t * K + lane];
+  u32x4 acc = u32x4{0u, 0u, 0u, 0u};
+  u32x4 v[2 * KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const int r = __builtin_amdgcn_readlane(myrow, j);
+    v[2 * j] = v[2 * j + 1] = u32x4{0u, 0u, 0u, 0u};
+    if (j < K && r >= 0) {
+      const u32x4 *row = (const u32x4 *)(buf + (size_t)r * row_bytes);
+      if (c0 < nch) v[2 * j] = __builtin_nontemporal_load(row + c0);
+      if (c1 < nch) v[2 * j + 1] = __builtin_nontemporal_load(row + c1);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2 * KMAX; ++i) acc ^= v[i];
+  if (acc.x == 0x9e3779b9u && acc.y == 0x7f4a7c15u && acc.z == 0xf39cc060u && acc.w == 0x5ced2c1du)
+    sink[(size_t)gw * 64 + lane] = acc;
+}
+
 int block_for(int row_bytes) { return 64 * ((row_bytes / 16 + 63) / 64); }
 
 }  // namespace
@@ -69,6 +103,28 @@ int moe_probe_ordered_write(int64_t nrows, int row_bytes, void *buf, void *strea
   if (blocks > 0x7fffffff) return -1;
   hipLaunchKernelGGL(probe_ordered_kernel, dim3((unsigned)blocks), dim3(block_for(row_bytes)), 0,
                      (hipStream_t)stream, nrows, row_bytes, (unsigned char *)buf);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// Read every row buf[dst_row[t, j]] (dst_row[t, j] >= 0) in the combine's launch shape: one wave
+// per (token, 2 KB slice), row_bytes a multiple of 16, at most 16384, K at most 16.  sink receives
+// T * ceil(row_bytes / 2048) * 64 16-byte words.  Returns 0, or -1 for bad arguments, -5 when the
+// launch fails.
+int moe_probe_gather_read(const int32_t *dst_row, int T, int K, int row_bytes, const void *buf, void *sink,
+                          void *stream) {
+  if (T < 0 || K <= 0 || K > 16 || row_bytes <= 0 || row_bytes % 16 || row_bytes > 16384 || !buf || !sink ||
+      (T > 0 && !dst_row))
+    return -1;
+  if ((((uintptr_t)buf | (uintptr_t)sink) & 15u) != 0) return -1;
+  if (T == 0) return 0;
+  const int nslice = (row_bytes / 16 + 127) / 128;
+  const dim3 grid((unsigned)((int64_t)T * nslice));
+  if (K <= 8)
+    hipLaunchKernelGGL(probe_gather_kernel<8>, grid, dim3(64), 0, (hipStream_t)stream, dst_row, K, row_bytes,
+                       (const unsigned char *)buf, nslice, (u32x4 *)sink);
+  else
+    hipLaunchKernelGGL(probe_gather_kernel<16>, grid, dim3(64), 0, (hipStream_t)stream, dst_row, K, row_bytes,
+                       (const unsigned char *)buf, nslice, (u32x4 *)sink);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
