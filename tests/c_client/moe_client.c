@@ -3,16 +3,18 @@
  *
  * usage: moe_client DIR
  *
- * DIR/shape.txt holds twelve or thirteen integers: T H K E P Z C Kc num_max
- * quant_mode has_mask smooth_rows [fused].  The inputs are raw little-endian files in DIR:
+ * DIR/shape.txt holds twelve to fourteen integers: T H K E P Z C Kc num_max
+ * quant_mode has_mask smooth_rows [path [max_workgroups]].  The inputs are raw little-endian files in DIR:
  * topk_idx.bin (int32 [T,K]), x.bin (bf16 [T,H]), w.bin (fp32 [T,K]),
  * y.bin (bf16 [rows,H], the expert outputs the combine reads), mask.bin (u8 [T],
  * when has_mask), smooth.bin (fp32 [smooth_rows,H], when smooth_rows > 0) and,
  * when Kc > 0, a1.bin, a2.bin, cv.bin (bf16 [Kc,H]).  The client allocates
  * device memory with the HIP runtime, runs moe_get_layout, moe_dispatch and
- * moe_combine through the C ABI of moe_get.h on the null stream (with fused
- * = 1, moe_layout_dispatch in place of the first two), and writes
- * every output next to the inputs (out_*.bin).  Exit status 0 on success.
+ * moe_combine through the C ABI of moe_get.h on the null stream (path 1:
+ * moe_layout_dispatch in place of the first two; path 2: moe_get_layout_noalloc,
+ * moe_dispatch_capped and moe_combine_capped on max_workgroups workgroups, with no
+ * workspace allocated), and writes every output next to the inputs (out_*.bin).
+ * Exit status 0 on success.
  */
 #define __HIP_PLATFORM_AMD__ 1
 #include <hip/hip_runtime_api.h>
@@ -85,8 +87,8 @@ static void check_moe(int s, const char *what) {
 }
 
 int main(int argc, char **argv) {
-  long v[13];
-  int i, has_mask, quant_mode, fused;
+  long v[14];
+  int i, has_mask, quant_mode, fused, max_wg;
   int64_t smooth_rows, rows;
   moe_get_shape_t sh;
   FILE *f;
@@ -102,6 +104,7 @@ int main(int argc, char **argv) {
   for (i = 0; i < 12; ++i)
     if (fscanf(f, "%ld", &v[i]) != 1) return 1;
   if (fscanf(f, "%ld", &v[12]) != 1) v[12] = 0;
+  if (fscanf(f, "%ld", &v[13]) != 1) v[13] = 0;
   fclose(f);
   sh.num_tokens = (int32_t)v[0];
   sh.hidden = (int32_t)v[1];
@@ -116,6 +119,7 @@ int main(int argc, char **argv) {
   has_mask = (int)v[10];
   smooth_rows = v[11];
   fused = (int)v[12];
+  max_wg = (int)v[13];
 
   if (moe_get_abi_version() != MOE_GET_ABI_VERSION) return 4;
   check_moe(moe_get_check_shape(&sh), "moe_get_check_shape");
@@ -125,7 +129,7 @@ int main(int argc, char **argv) {
     const size_t NS = (size_t)(sh.zero_expert_num + sh.copy_expert_num + sh.const_expert_num);
     const size_t Kc = (size_t)sh.const_expert_num;
     const size_t cap = (size_t)moe_get_recv_capacity(&sh);
-    const size_t wsb = moe_get_workspace_size(&sh);
+    const size_t wsb = fused == 2 ? 0 : moe_get_workspace_size(&sh);
     const size_t qbytes = quant_mode == MOE_QUANT_NONE ? 2 : 1;
     void *topk = read_file("topk_idx", T * K * 4), *x = read_file("x", T * H * 2);
     void *w = read_file("w", T * K * 4);
@@ -135,7 +139,7 @@ int main(int argc, char **argv) {
     void *d_recv = dev_buf(NULL, E * P * 4), *d_spec = dev_buf(NULL, NS * 4);
     void *d_ntpr = dev_buf(NULL, P * 4), *d_roff = dev_buf(NULL, (P + 1) * 4);
     void *d_itr = dev_buf(NULL, T * P), *d_dst = dev_buf(NULL, T * K * 4);
-    void *d_src = dev_buf(NULL, cap * 4), *d_status = dev_buf(NULL, 4), *d_ws = dev_buf(NULL, wsb);
+    void *d_src = dev_buf(NULL, cap * 4), *d_status = dev_buf(NULL, 4), *d_ws = wsb ? dev_buf(NULL, wsb) : NULL;
     void *d_ex = dev_buf(NULL, cap * H * qbytes), *d_ds = dev_buf(NULL, cap * 4);
     void *d_ew = dev_buf(NULL, cap * 4), *d_out = dev_buf(NULL, T * H * 2);
     int32_t n_rows = 0;
@@ -163,7 +167,19 @@ int main(int argc, char **argv) {
     }
     CHECK_HIP(hipMemset(d_status, 0, 4));
 
-    if (fused) {
+    if (fused == 2) {
+      if (wsb != 0 || moe_get_workspace_size(&sh) > moe_get_noalloc_scratch_bytes()) return 5;
+      check_moe(moe_get_layout_noalloc(&sh, 0, (const int32_t *)d_topk, (const uint8_t *)d_mask, (int32_t *)d_cnt,
+                                       (int32_t *)d_eoff, (int32_t *)d_recv, (int32_t *)d_spec, (int32_t *)d_ntpr,
+                                       (int32_t *)d_roff, (uint8_t *)d_itr, (int32_t *)d_dst, (int32_t *)d_src,
+                                       (uint32_t *)d_status, NULL),
+                "moe_get_layout_noalloc");
+      check_moe(moe_dispatch_capped(&sh, max_wg, quant_mode, (const uint16_t *)d_x, (const float *)d_smooth,
+                                    (int32_t)smooth_rows, (const float *)d_w, (const int32_t *)d_topk,
+                                    (const int32_t *)d_dst, d_ex,
+                                    quant_mode == MOE_QUANT_DYNAMIC_INT8 ? (float *)d_ds : NULL, (float *)d_ew, NULL),
+                "moe_dispatch_capped");
+    } else if (fused) {
       check_moe(moe_layout_dispatch(&sh, 0, quant_mode, (const int32_t *)d_topk, (const uint8_t *)d_mask,
                                     (const uint16_t *)d_x, (const float *)d_smooth, (int32_t)smooth_rows,
                                     (const float *)d_w, (int32_t *)d_cnt, (int32_t *)d_eoff, (int32_t *)d_recv,
@@ -189,11 +205,11 @@ int main(int argc, char **argv) {
     y = read_file("y", (size_t)rows * H * 2);
     d_y = dev_buf(y, (size_t)rows * H * 2);
     free(y);
-    check_moe(moe_combine(&sh, (const uint16_t *)d_y, (const int32_t *)d_topk, (const float *)d_w,
-                          (const uint8_t *)d_mask, (const int32_t *)d_dst, (const uint16_t *)d_x,
-                          (const uint16_t *)d_a1, (const uint16_t *)d_a2, (const uint16_t *)d_cv,
-                          (uint16_t *)d_out, NULL),
-              "moe_combine");
+    check_moe(moe_combine_capped(&sh, fused == 2 ? max_wg : 0, (const uint16_t *)d_y, (const int32_t *)d_topk,
+                                 (const float *)d_w, (const uint8_t *)d_mask, (const int32_t *)d_dst,
+                                 (const uint16_t *)d_x, (const uint16_t *)d_a1, (const uint16_t *)d_a2,
+                                 (const uint16_t *)d_cv, (uint16_t *)d_out, NULL),
+              "moe_combine_capped");
     CHECK_HIP(hipDeviceSynchronize());
 
     save("num_tokens_per_expert", d_cnt, E * 4);
@@ -210,8 +226,8 @@ int main(int argc, char **argv) {
     save("dynamic_scales", d_ds, (size_t)rows * 4);
     save("expand_weights", d_ew, (size_t)rows * 4);
     save("out", d_out, T * H * 2);
-    printf("moe_client ok: T=%zu H=%zu K=%zu E=%zu P=%zu rows=%d quant=%d fused=%d\n", T, H, K, E, P, n_rows,
-           quant_mode, fused);
+    printf("moe_client ok: T=%zu H=%zu K=%zu E=%zu P=%zu rows=%d quant=%d path=%d max_workgroups=%d\n", T, H, K, E,
+           P, n_rows, quant_mode, fused, max_wg);
   }
   return 0;
 }

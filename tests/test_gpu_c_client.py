@@ -34,7 +34,10 @@ def _read(d, name, dtype, shape):
     return a.reshape(shape)
 
 
-def _run(tmp, w, quant_mode, num_max=0, smooth_rows=None, fused=False):
+def _run(tmp, w, quant_mode, num_max=0, smooth_rows=None, fused=False, path=None, max_workgroups=0):
+    """path 0: layout + dispatch + combine; 1: layout_dispatch + combine; 2: layout_noalloc +
+    dispatch_capped + combine_capped on max_workgroups workgroups"""
+    path = (1 if fused else 0) if path is None else path
     T, H, K, E, P, Z, C, Kc = (w[k] for k in ("T", "H", "K", "E", "P", "Z", "C", "Kc"))
     osh = oracle.make_shape(T, H, K, E, P, Z, C, Kc, num_max)
     mask = w.get("mask")
@@ -54,7 +57,7 @@ def _run(tmp, w, quant_mode, num_max=0, smooth_rows=None, fused=False):
     d = str(tmp)
     with open(os.path.join(d, "shape.txt"), "w") as f:
         f.write(" ".join(str(int(v)) for v in (T, H, K, E, P, Z, C, Kc, num_max, quant_mode,
-                                                 mask is not None, srows, fused)) + "\n")
+                                                 mask is not None, srows, path, max_workgroups)) + "\n")
     _write(d, "topk_idx", w["topk_idx"].astype(np.int32))
     _write(d, "x", w["x"])
     _write(d, "w", w["topk_weights"].astype(np.float32))
@@ -68,7 +71,7 @@ def _run(tmp, w, quant_mode, num_max=0, smooth_rows=None, fused=False):
         _write(d, "a2", w["alpha2"])
         _write(d, "cv", w["const_v"])
     print(f"[c-client] T={T} H={H} K={K} E={E} P={P} Z={Z} C={C} Kc={Kc} quant={quant_mode} "
-          f"smooth_rows={srows} mask={mask is not None} fused={fused}", flush=True)
+          f"smooth_rows={srows} mask={mask is not None} path={path} max_workgroups={max_workgroups}", flush=True)
     r = subprocess.run([_client(), d], capture_output=True, text=True, timeout=90)
     print(r.stdout, r.stderr, flush=True)
     assert r.returncode == 0, r.stderr
@@ -120,3 +123,12 @@ def test_c_client_ll_decode_share(tmp_path, fused):
     w = dict(T=c["T"], H=c["H"], K=c["K"], E=c["E"], P=c["P"], Z=0, C=0, Kc=0, x=inp["x"],
              topk_idx=inp["topk_idx"], topk_weights=inp["topk_weights"], smooth=inp["smooth"])
     _run(tmp_path, w, 2, num_max=c["num_max"], fused=fused)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("seed,quant_mode,cap", [(4, 0, 3), (6, 2, 50), (9, 1, 1)])
+def test_c_client_noalloc_and_capped(tmp_path, seed, quant_mode, cap):
+    # moe_get_layout_noalloc (no workspace anywhere in the process), moe_dispatch_capped and
+    # moe_combine_capped, driven from plain C
+    w = fuzz_world(seed, Z=1, C=1, Kc=1)
+    _run(tmp_path, w, quant_mode, path=2, max_workgroups=cap)

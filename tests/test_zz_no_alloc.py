@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import combine_moe_get_amd as mg
+from combine_moe_get_amd import workloads
 from tests import _gpu as G
 
 pytestmark = pytest.mark.gpu
@@ -72,3 +73,65 @@ def test_noalloc_refuses_shapes_beyond_its_scratch():
     assert ei.value.status == -6
     torch.cuda.synchronize()
     assert torch.all(out.dst_row == -9), "a refused call launched"
+
+
+def test_noalloc_layout_inside_a_captured_graph():
+    # the caller this entry point is for: a whole layer (allocation-free layout, dispatch, combine)
+    # captured once in a graph and replayed on new inputs copied into the captured tensors, with
+    # eager work between replays; every replay equals the same layer run eagerly through
+    # moe_get_layout_ex with a caller-owned workspace
+    T, H, K, E, P = 2048, 1024, 8, 64, 16  # 16384 slots: the two-launch layout, which uses the scratch
+    shape = mg.make_shape(T, H, K, E, P)
+    assert mg.layout_launches(shape) == 2
+    topk = torch.empty((T, K), dtype=torch.int32, device=G.DEV)
+    w = torch.empty((T, K), dtype=torch.float32, device=G.DEV)
+    x = torch.empty((T, H), dtype=torch.bfloat16, device=G.DEV)
+    y = torch.empty((T * K, H), dtype=torch.bfloat16, device=G.DEV)
+    lay = mg.alloc_layout(shape, G.DEV)
+    ex = torch.zeros((T * K, H), dtype=torch.int8, device=G.DEV)
+    ds = torch.zeros(T * K, dtype=torch.float32, device=G.DEV)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=G.DEV)
+    calls = (mg.prepare_layout_noalloc(shape, topk, None, out=lay),
+             mg.prepare_dispatch(shape, 2, x, lay.dst_row, None, w, topk, ex, ds),
+             mg.prepare_combine(shape, y, topk, w, lay.dst_row, out=out))
+
+    def fill(seed):
+        r = np.random.default_rng(seed)
+        topk.copy_(G.dev(np.argsort(r.random((T, E)), axis=1)[:, :K].astype(np.int32)))
+        w.copy_(G.dev(r.standard_normal((T, K)).astype(np.float32)))
+        x.copy_(G.dev(workloads.f32_to_bf16_bits(r.standard_normal((T, H)).astype(np.float32))))
+        y.copy_(G.dev(workloads.expert_out_normal(T * K, H, seed=seed)))
+        torch.cuda.synchronize()
+
+    def reference():
+        rl = mg.layout(shape, topk)
+        rex, rds, _ = mg.dispatch(shape, 2, x, rl.dst_row, None, w, topk)
+        rout = mg.combine(shape, y, topk, w, rl.dst_row)
+        torch.cuda.synchronize()
+        n = int(rl.expert_offsets[-1])
+        return rl, rex[:n].clone(), rds[:n].clone(), rout.clone(), n
+
+    fill(1)
+    for c in calls:  # eager first: the scratch address is looked up outside the capture
+        c()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        st = torch.cuda.current_stream()
+        for c in calls:
+            c(st)
+    for rep in range(3):
+        fill(10 + rep)
+        lay.dst_row.fill_(-7)
+        out.zero_()
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        rl, rex, rds, rout, n = reference()
+        print(f"[noalloc graph] replay {rep}: rows={n}", flush=True)
+        for name, a, b in zip(rl._fields, rl, lay):
+            if name == "src_info":
+                a, b = a[:n], b[:n]
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager layout"
+        assert torch.equal(ex[:n], rex) and torch.equal(ds[:n].view(torch.int32), rds.view(torch.int32))
+        assert torch.equal(out.view(torch.int16), rout.view(torch.int16)), f"replay {rep}: combine differs"
