@@ -307,13 +307,19 @@ int moe_get_layout_noalloc(const moe_get_shape_t *shape, int64_t rank_stride, co
   const int st = check_shape(shape);
   if (st != MOE_OK) return st;
   if (ws_layout(shape).total > kScratchBytes) return MOE_ERR_SCRATCH;
+  // every argument is checked before the runtime is asked for anything (an aligned stand-in for
+  // the scratch address first, then the real one)
+  LayoutArgs a;
+  int ast = layout_args(shape, rank_stride, topk_idx, x_active_mask, num_tokens_per_expert, expert_offsets,
+                        recv_counts, special_counts, num_tokens_per_rank, rank_offsets, is_token_in_rank, dst_row,
+                        src_info, status_dev, (void *)kAlign, kScratchBytes, a);
+  if (ast != MOE_OK) return ast;
   void *ws = nullptr;
   const int sst = scratch_on((hipStream_t)stream, &ws);
   if (sst != MOE_OK) return sst;
-  LayoutArgs a;
-  const int ast = layout_args(shape, rank_stride, topk_idx, x_active_mask, num_tokens_per_expert, expert_offsets,
-                              recv_counts, special_counts, num_tokens_per_rank, rank_offsets, is_token_in_rank,
-                              dst_row, src_info, status_dev, ws, kScratchBytes, a);
+  ast = layout_args(shape, rank_stride, topk_idx, x_active_mask, num_tokens_per_expert, expert_offsets, recv_counts,
+                    special_counts, num_tokens_per_rank, rank_offsets, is_token_in_rank, dst_row, src_info,
+                    status_dev, ws, kScratchBytes, a);
   if (ast != MOE_OK) return ast;
   return launch_layout(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

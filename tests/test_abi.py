@@ -122,3 +122,37 @@ def test_layout_launches():
     assert mg.layout_launches(mg.make_shape(1024, 7168, 16, 256, 2)) == 2  # 16384 slots
     with pytest.raises(mg.MoeGetError):
         mg.layout_launches(mg.make_shape(100, 7168, 8, 256, 32))  # T not a multiple of P
+
+
+def test_argument_errors_return_before_any_device_work():
+    # the host-side failure paths of the C ABI, forced from the host on a machine without a GPU:
+    # each call must return its status before asking the HIP runtime for anything
+    L = mg.lib()
+    ok = mg.make_shape(64, 64, 4, 8, 2, 0, 1, 0)  # one copy expert
+    p = ctypes.c_void_p(256)  # an aligned, never dereferenced stand-in for a device pointer
+    n = None
+    # combine with a copy expert but no ori_x
+    assert L.moe_combine(ctypes.byref(ok), p, p, p, n, p, n, n, n, n, p, n) == -1
+    # bad quant mode; per-expert scales without topk_idx; negative grid cap
+    assert L.moe_dispatch(ctypes.byref(ok), 3, p, n, 0, n, n, p, p, n, n, n) == -1
+    assert L.moe_dispatch(ctypes.byref(ok), 2, p, p, 8, n, n, p, p, p, n, n) == -1
+    assert L.moe_dispatch_capped(ctypes.byref(ok), -1, 0, p, n, 0, n, n, p, p, n, n, n) == -1
+    assert L.moe_combine_capped(ctypes.byref(ok), -1, p, p, p, n, p, p, n, n, n, p, n) == -1
+    # misaligned rows
+    assert L.moe_dispatch(ctypes.byref(ok), 0, p, n, 0, n, n, p, ctypes.c_void_p(258), n, n, n) == -1
+    # layout: no workspace; a rank window below capacity; BS above num_max
+    outs = [p] * 9
+    assert L.moe_get_layout(ctypes.byref(ok), p, n, *outs, n, n, 0, n) == -1
+    cap = mg.rank_capacity(ok)
+    assert L.moe_get_layout_ex(ctypes.byref(ok), cap - 1, p, n, *outs, n, p, 1 << 20, n) == -3
+    assert L.moe_get_layout(ctypes.byref(mg.make_shape(64, 64, 4, 8, 2, num_max=16)), p, n, *outs, n, p,
+                            1 << 20, n) == -3
+    # the allocation-free layout: a missing output, then a shape whose workspace exceeds the scratch
+    bad_outs = [p] * 8 + [n]
+    assert L.moe_get_layout_noalloc(ctypes.byref(ok), 0, p, n, *bad_outs, n, n) == -1
+    big = mg.make_shape(2048, 64, 4, 2048, 2048)
+    assert L.moe_get_layout_noalloc(ctypes.byref(big), 0, p, n, *outs, n, n) == -6
+    # T = 0 does nothing and succeeds without touching any pointer
+    empty = mg.make_shape(0, 64, 4, 8, 2)
+    assert L.moe_dispatch(ctypes.byref(empty), 0, n, n, 0, n, n, n, n, n, n, n) == 0
+    assert L.moe_combine(ctypes.byref(empty), n, n, n, n, n, n, n, n, n, n, n) == 0
