@@ -402,6 +402,59 @@ def run_dbo(args):
                       "results": results}), flush=True)
 
 
+def run_write_sweep(args):
+    """Write-pattern sweep with libmoe_hbm_probe.so: rows of R bytes (1-16 KB) stored at randomly
+    permuted row slots (eight rows per workgroup, as the dispatch's copies of one token), against the
+    same bytes stored in address order; about 940 MB per launch, far beyond the 256 MB Infinity Cache.
+    Prints one JSON line."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    plib = ctypes.CDLL(PROBE_LIB_PATH)
+    plib.moe_probe_scatter_write.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_void_p, ctypes.c_void_p]
+    plib.moe_probe_ordered_write.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    total = 940 << 20
+    buf = torch.empty(total + (1 << 20), dtype=torch.uint8, device=dev)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    gen = torch.Generator(device=dev).manual_seed(args.seed)
+    res = []
+    for R in (1024, 2048, 4096, 7168, 8192, 14336, 16384):
+        nrows = total // R // 8 * 8
+        perm = torch.randperm(nrows, generator=gen, device=dev).to(torch.int32).view(nrows // 8, 8).contiguous()
+
+        def t_of(fn):
+            fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(5):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b) * 1e3)
+            return float(np.median(ts))
+
+        def scat():
+            if plib.moe_probe_scatter_write(ctypes.c_void_p(perm.data_ptr()), nrows // 8, 8, R,
+                                            ctypes.c_void_p(buf.data_ptr()), st) != 0:
+                raise RuntimeError("probe refused its arguments")
+
+        def ordered():
+            if plib.moe_probe_ordered_write(nrows, R, ctypes.c_void_p(buf.data_ptr()), st) != 0:
+                raise RuntimeError("probe refused its arguments")
+
+        ts, to = t_of(scat), t_of(ordered)
+        b = nrows * R
+        res.append(dict(row_bytes=R, bytes=b, random_slots_us=round(ts, 1), random_slots_GBps=round(b / ts / 1e3, 1),
+                        address_order_us=round(to, 1), address_order_GBps=round(b / to / 1e3, 1)))
+        print(json.dumps(res[-1]), file=sys.stderr, flush=True)
+        del perm
+    print(json.dumps({"metric": "HBM write rate by row size: rows at random slots vs address order",
+                      "unit": "GB/s", "n_gpus": 1, "results": res}), flush=True)
+
+
 MALL_BYTES = 256 << 20  # MI355X Infinity Cache
 PROBE_LIB_PATH = os.path.join(ROOT, "combine_moe_get_amd", "libmoe_hbm_probe.so")
 # what the path moves and computes in, per quant mode (the JSON line's dtype)
@@ -786,6 +839,9 @@ def main():
     ap.add_argument("--no-write-probe", action="store_true",
                     help="skip the access-pattern probes (the dispatch's row map, stores only, vs address order; "
                          "the combine's rows, reads only)")
+    ap.add_argument("--write-sweep", action="store_true",
+                    help="write-pattern sweep over row sizes (random slots vs address order) instead of the step "
+                         "benchmark (prints its own JSON line)")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the other named workloads (each timed like the headline one, summarized in "
                          "the line's 'workloads' key)")
@@ -800,6 +856,9 @@ def main():
 
     if args.dbo:
         run_dbo(args)
+        return
+    if args.write_sweep:
+        run_write_sweep(args)
         return
 
     import torch
