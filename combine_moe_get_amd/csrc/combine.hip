@@ -15,7 +15,9 @@
 // loads of both its chunks for every routed slot before the first FMA.  One
 // exception: rows of 7 slices (6144 < H <= 7168) with many tokens, no mask and
 // no special experts run one wave per whole token that writes its row last
-// (combine_row_kernel), which measured faster there and only there.
+// (combine_row_kernel), which measured faster there and only there.  moe_combine_capped
+// runs the slice kernel on at most max_workgroups workgroups that walk the same items
+// with a grid stride (same per-item code, identical results).
 #include "moe_internal.hpp"
 
 namespace moe {

@@ -20,6 +20,9 @@
 //  - int8 with per-expert scales: one workgroup per token (dynamic) or per
 //    (token, expert-id parity) (static), the copies quantized one at a time (see
 //    dispatch_quant_expert_kernel).
+// Every kernel also has a looping form for moe_dispatch_capped: a grid of at most
+// max_workgroups workgroups walks the same work items with a grid stride (the per-item
+// code is shared, so the results are identical).
 // Loads are ordinary (the row is read once, K stores reuse it from VGPRs; the bf16
 // copy reads through a buffer resource, row_load).
 // Receive rows are written once and read by a later kernel: the int8 codes are
@@ -154,7 +157,9 @@ __global__ void __launch_bounds__(512) dispatch_quant_kernel(DispatchArgs a) {
 // best for static codes (109 us against 117 for G = 1, 112 for G = 4 at T=4096,
 // H=7168, top-8); with the dynamic scale's block-wide amax per copy, G = 1 is
 // (121 against 127 for G = 2) -- splitting a token's copies adds barriers to fewer
-// copies per block.  G = 8 loses in both (the token row is fetched by every XCD).
+// copies per block.  G = 4 and G = 8 lose in both, also when a block requests the token
+// row only after it knows it has a copy (G = 8: 175-185 against 134-147 us dynamic): each
+// block then has one or two copies and its chain of dependent loads is not hidden.
 // Copies are quantized one at a time with the codes kept in registers across the
 // block-wide amax, so each scale row is read once per copy.
 template <int MODE>
