@@ -1,9 +1,12 @@
 """Benchmark of one MoE layer's data path on one MI355X: routing layout +
 dispatch + combine, timed through the C ABI.
 
-A step is one pass of the whole path over one batch: moe_get_layout (2
-kernels), moe_dispatch (1 kernel), moe_combine (1 kernel), with every input
-already resident in HBM.  The expert computation between dispatch and combine
+A step is one pass of the whole path over one batch: moe_layout_dispatch
+(the layout's 2 kernels, which also read the token rows ahead into the
+Infinity Cache, then the dispatch kernel; one fused kernel for T * K <= 8192)
+and moe_combine (1 kernel), with every input already resident in HBM.  The
+same work as three calls (moe_get_layout, moe_dispatch, moe_combine) is timed
+beside it, with events between the calls for the per-call times.  The expert computation between dispatch and combine
 is not part of the path; a stand-in expert output (the dequantized dispatched
 rows, or the dispatched bf16 rows) is prepared once, untimed.
 
@@ -554,7 +557,16 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False,
                                                out=g["lay"], expand_x=g["ex"], dynamic_scales=g["ds"],
                                                workspace=g["ws"], rank_stride=A)
 
-    def step(g, ev=None, st=None):
+    # the timed step is the library's layer path: moe_layout_dispatch (layout and dispatch in one
+    # call; one kernel for T * K <= 8192, else the layout kernels, which also read the token rows
+    # ahead into the Infinity Cache, then the dispatch) and moe_combine
+    def step(g, st=None):
+        st = stream if st is None else st
+        g["c_ld"](st)
+        g["c_com"](st)
+
+    # the same work as three calls, events between them: what each call takes inside a step
+    def step3(g, ev=None, st=None):
         st = stream if st is None else st
         if ev is not None:
             ev[0].record(st)
@@ -570,6 +582,7 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False,
 
     for i in range(args.warmup):
         step(gsets[i % len(gsets)])
+        step3(gsets[i % len(gsets)])
     torch.cuda.synchronize()
 
     graphs = None
@@ -610,10 +623,18 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False,
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
 
-    # per-call timing inside steps: the same steps with events between the calls
+    # the same steps as three calls, timed alike (nothing between the calls)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step3(gsets[i % len(gsets)])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    three_ms = t_start.elapsed_time(t_end) / args.steps
+
+    # per-call timing inside steps: the three-call steps with events between the calls
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
-        step(gsets[i % len(gsets)], evs[i])
+        step3(gsets[i % len(gsets)], evs[i])
     torch.cuda.synchronize()
     lay_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     dis_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
@@ -695,25 +716,13 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False,
             what="stores only (no reads): every receive row of the dispatch's own row map, one workgroup per "
                  "token as the int8 dispatch, against the same bytes stored in address order")
 
-    # the step with layout + dispatch through moe_layout_dispatch (one kernel for T * K <= 8192)
-    fused = None
-    if graphs is None and headline:
-        def step_fused(g):
-            g["c_ld"](stream)
-            g["c_com"](stream)
-        for i in range(args.warmup):
-            step_fused(gsets[i % len(gsets)])
-        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        f0.record(stream)
-        for i in range(args.steps):
-            step_fused(gsets[i % len(gsets)])
-        f1.record(stream)
-        torch.cuda.synchronize()
-        k_ld = kernel_avg_ms(lambda g: g["c_ld"](stream))
-        fused = dict(us_per_layer=round(f0.elapsed_time(f1) / args.steps * 1e3, 2),
-                     layout_dispatch_kernel_us=round(k_ld * 1e3, 2),
-                     layout_dispatch_launches=mg.layout_dispatch_launches(shape))
+    # moe_layout_dispatch alone, and the step as three calls (moe_get_layout, moe_dispatch,
+    # moe_combine; the dispatch then reads the token rows from HBM)
+    k_ld = kernel_avg_ms(lambda g: g["c_ld"](stream))
+    three_call = dict(us_per_layer=round(three_ms * 1e3, 2), layout_dispatch_call_us=round(k_ld * 1e3, 2),
+                      layout_dispatch_launches=mg.layout_dispatch_launches(shape),
+                      what="us_per_layer: the step as moe_get_layout + moe_dispatch + moe_combine (timed like the "
+                           "headline step); layout_dispatch_call_us: moe_layout_dispatch back to back")
 
     n_avg = float(np.mean([g["n"] for g in gsets]))
     cb_d = dispatch_comm_bytes(n_avg, H, qm)
@@ -788,8 +797,7 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False,
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    if fused is not None:
-        line["fused_layout_dispatch"] = fused
+    line["three_call_step"] = three_call
     if row_probe is not None:
         line["row_placement_probe"] = row_probe
     if write_probe is not None:
@@ -882,7 +890,7 @@ def main():
             kernel_us={k: v["kernel_us"] for k, v in sh["kernels"].items()},
             in_step_us_median={k: v["in_step_us_median"] for k, v in sh["kernels"].items()},
             layout_launches=sh["kernels"]["layout"]["launches"],
-            fused_layout_dispatch=sh.get("fused_layout_dispatch"))
+            three_call_step=sh.get("three_call_step"))
     overrides = (args.tokens, args.ranks, args.quant, args.smooth) != (None, None, None, None) or \
         args.rank_stride not in ("0", 0) or args.graph
     if not args.no_workloads and not overrides:

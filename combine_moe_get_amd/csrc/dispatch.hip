@@ -41,6 +41,7 @@ namespace moe {
 // stores then): 104.2-104.6 us against 105.6-106.5 us for 1 KB slices in four-wave workgroups.
 // With buffer-resource loads and sc1 stores (98-100 us), 1, 3 and 4 KB slices measured
 // 102.6-103.5, 104.7-105.3 and 106.2-106.7 us against 100.1-100.8 us for 2 KB in one run.
+template <bool NT>
 __device__ __forceinline__ void dispatch_copy_item(const DispatchArgs &a, int nslice, int gw) {
   const int lane = threadIdx.x;
   const int t = gw / nslice, sl = gw - t * nslice;
@@ -64,20 +65,29 @@ __device__ __forceinline__ void dispatch_copy_item(const DispatchArgs &a, int ns
     const int j = __builtin_ctzll(valid);
     valid &= valid - 1;
     void *dst = (uint16_t *)a.expand_x + (size_t)readlane(myrow, j) * H;
-    if (c0 < nch) row_store_sc1(v0, dst, 2 * H, c0 * 16);
-    if (c1 < nch) row_store_sc1(v1, dst, 2 * H, c1 * 16);
+    if (NT) {
+      if (c0 < nch) __builtin_nontemporal_store(v0, (u32x4 *)dst + c0);
+      if (c1 < nch) __builtin_nontemporal_store(v1, (u32x4 *)dst + c1);
+    } else {
+      if (c0 < nch) row_store_sc1(v0, dst, 2 * H, c0 * 16);
+      if (c1 < nch) row_store_sc1(v1, dst, 2 * H, c1 * 16);
+    }
   }
   if (write_w) a.expand_w[myrow] = a.w ? a.w[(size_t)t * K + lane] : 1.0f;
 }
 
 // items: T * nslice (token, slice) pairs.  LOOP: a grid smaller than that (a capped launch) walks
-// them with a grid stride; otherwise one workgroup per item (the loop costs registers: 12 -> 18)
-template <bool LOOP>
+// them with a grid stride; otherwise one workgroup per item (the loop costs registers: 12 -> 18).
+// NT: non-temporal stores, used when the token rows were just read ahead into the Infinity Cache
+// (moe_layout_dispatch): there the copy measured faster with them (workload T=4096, H=7168, top-8,
+// Zipf: 194.9 against 196.3 us per layer with sc1 stores; at T=8192, H=4096: 224.7 against 228.0),
+// while without the read-ahead sc1 stores are faster (101.5 against 104 us for the copy alone).
+template <bool LOOP, bool NT>
 __global__ void __launch_bounds__(64) dispatch_copy_kernel(DispatchArgs a, int nslice, int items) {
   if constexpr (LOOP) {
-    for (int gw = blockIdx.x; gw < items; gw += gridDim.x) dispatch_copy_item(a, nslice, gw);
+    for (int gw = blockIdx.x; gw < items; gw += gridDim.x) dispatch_copy_item<NT>(a, nslice, gw);
   } else {
-    dispatch_copy_item(a, nslice, blockIdx.x);
+    dispatch_copy_item<NT>(a, nslice, blockIdx.x);
   }
 }
 
@@ -230,14 +240,17 @@ __global__ void __launch_bounds__(512) dispatch_quant_expert_kernel(DispatchArgs
 
 template <bool LOOP>
 static void launch_dispatch_grid(const DispatchArgs &a, int quant_mode, bool per_expert, hipStream_t stream,
-                                 int max_wg) {
+                                 int max_wg, bool rows_cached) {
   // grid over `items` work items: one workgroup per item, or at most max_wg (LOOP)
   auto grid = [max_wg](int64_t items) { return dim3((unsigned)(LOOP && items > max_wg ? max_wg : items)); };
   const int nch = a.H / 8;
   if (quant_mode == 0) {
     const int nslice = (nch + 127) / 128;
     const int64_t items = (int64_t)a.T * nslice;
-    hipLaunchKernelGGL(dispatch_copy_kernel<LOOP>, grid(items), dim3(64), 0, stream, a, nslice, (int)items);
+    if (rows_cached)
+      hipLaunchKernelGGL((dispatch_copy_kernel<LOOP, true>), grid(items), dim3(64), 0, stream, a, nslice, (int)items);
+    else
+      hipLaunchKernelGGL((dispatch_copy_kernel<LOOP, false>), grid(items), dim3(64), 0, stream, a, nslice, (int)items);
     return;
   }
   const int pairs = (nch + 1) / 2;  // <= 512 for H <= 8192
@@ -254,12 +267,12 @@ static void launch_dispatch_grid(const DispatchArgs &a, int quant_mode, bool per
 }
 
 hipError_t launch_dispatch(const DispatchArgs &a, int quant_mode, bool per_expert, hipStream_t stream,
-                           int max_wg) {
+                           int max_wg, bool rows_cached) {
   if (a.T == 0) return hipSuccess;
   if (max_wg > 0)
-    launch_dispatch_grid<true>(a, quant_mode, per_expert, stream, max_wg);
+    launch_dispatch_grid<true>(a, quant_mode, per_expert, stream, max_wg, rows_cached);
   else
-    launch_dispatch_grid<false>(a, quant_mode, per_expert, stream, 0);
+    launch_dispatch_grid<false>(a, quant_mode, per_expert, stream, 0, rows_cached);
   return hipGetLastError();
 }
 

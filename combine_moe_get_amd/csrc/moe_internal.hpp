@@ -125,7 +125,36 @@ struct LayoutArgs {
   int32_t *ws_special;   // [P m][NS] per sub-chunk: special slots per id
   int32_t mt;            // 64-bit words per wave of the count kernel's LDS match tables; set by the launcher
   uint32_t divL, divK, divBSv, divE;  // div_magic of L, K, BSv and E: see fast_div
+  // read-ahead of the dispatch's token rows (layout + dispatch in one call): pf_wgs extra
+  // workgroups of the count kernel read bytes [0, pf_half) of pf, as many of the scan kernel
+  // [pf_half, pf_bytes), so the rows sit in the Infinity Cache when the dispatch reads them.
+  // pf_wgs = 0: no extra workgroups.
+  const void *pf;
+  int64_t pf_half, pf_bytes;
+  int32_t pf_wgs;
 };
+
+// Read bytes [lo, hi) of buf (16-byte aligned, hi - lo a multiple of 16) with ordinary loads,
+// workgroup wg of nwg, eight 16-byte loads per thread in flight: the lines are left in the caches
+// for a later kernel.  Nothing is stored; an empty asm statement consumes the loaded values so
+// the loads are kept.
+__device__ __forceinline__ void read_ahead(const void *buf, int64_t lo, int64_t hi, int wg, int nwg) {
+  const u32x4 *p = (const u32x4 *)((const unsigned char *)buf + lo);
+  const int64_t n = (hi - lo) >> 4;
+  const int64_t step = (int64_t)nwg * blockDim.x;
+  u32x4 acc = u32x4{0u, 0u, 0u, 0u};
+  for (int64_t i = (int64_t)wg * blockDim.x + threadIdx.x; i < n; i += 8 * step) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t j = i + u * step;
+      v[u] = j < n ? p[j] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u];
+  }
+  asm volatile("" ::"v"(acc.x), "v"(acc.y), "v"(acc.z), "v"(acc.w));
+}
 
 // Division by a divisor d fixed for the whole call, as a multiply-high: m = div_magic(d) =
 // ceil(2^32 / d) (0 for d = 1) and n / d = umulhi(n, m) for 0 <= n with n d < 2^32 (then
@@ -177,9 +206,11 @@ hipError_t launch_layout_dispatch(const LayoutArgs &a, const DispatchArgs &d, in
                                   hipStream_t stream);
 int layout_dispatch_launch_count(const LayoutArgs &a);
 // max_wg > 0: launch at most that many workgroups, each walking several work items (a capped
-// grid, which leaves the rest of the GPU to kernels running beside it); 0: one per item
+// grid, which leaves the rest of the GPU to kernels running beside it); 0: one per item.
+// rows_cached: the token rows were just read ahead into the caches (the bf16 copy then stores
+// non-temporally)
 hipError_t launch_dispatch(const DispatchArgs &a, int quant_mode, bool per_expert, hipStream_t stream,
-                           int max_wg = 0);
+                           int max_wg = 0, bool rows_cached = false);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream, int max_wg = 0);
 
 // LDS bytes of the layout count kernel and its waves per block
