@@ -707,6 +707,26 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False,
                           what="reads only: the combine's expert-output rows gathered in its launch shape (one wave "
                                "per token and 2 KB slice, non-temporal loads), no output rows written")
         del sink
+        # the combine's reads and writes with XOR in place of its arithmetic, on its row map and on
+        # T K rows read in address order (outputs to a buffer of their own)
+        if hasattr(plib, "moe_probe_reduce") and gsets[0]["y"].shape[0] >= T * K:
+            plib.moe_probe_reduce.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+            pout = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+            k_gr = kernel_avg_ms(lambda g: probe_call(plib.moe_probe_reduce(
+                ctypes.c_void_p(g["lay"].dst_row.data_ptr()), T, K, 2 * H, ctypes.c_void_p(g["y"].data_ptr()),
+                ctypes.c_void_p(pout.data_ptr()), 1, st_ptr)))
+            k_sr = kernel_avg_ms(lambda g: probe_call(plib.moe_probe_reduce(
+                None, T, K, 2 * H, ctypes.c_void_p(g["y"].data_ptr()), ctypes.c_void_p(pout.data_ptr()), 0, st_ptr)))
+            del pout
+            gb = rbytes + T * 2 * H
+            sb = float(T * K + T) * 2 * H
+            read_probe["reduce"] = dict(
+                gathered_us=round(k_gr * 1e3, 2), gathered_GBps=round(gb / 1e9 / (k_gr * 1e-3), 1),
+                address_order_us=round(k_sr * 1e3, 2), address_order_GBps=round(sb / 1e9 / (k_sr * 1e-3), 1),
+                what="the combine's reads and writes (K rows in, one row out per token, 2 KB slice per wave, "
+                     "non-temporal) with XOR instead of its arithmetic: on the combine's row map, and on the "
+                     "T K rows in address order")
         wbytes = float(np.mean([g["n"] for g in gsets])) * rowb
         write_probe = dict(
             row_bytes=rowb, bytes_per_launch=int(wbytes),

@@ -8,7 +8,9 @@
 // stored by all lanes), and (b) in address order (one workgroup per row, in row order),
 // so the benchmark can report what HBM accepts for each pattern next to the dispatch itself.
 // Stores are non-temporal, as the int8 dispatch's.  The gather probe is the combine's read side
-// alone: the same rows read in the combine's launch shape, with no output rows written.
+// alone: the same rows read in the combine's launch shape, with no output rows written; the
+// reduce probe is the combine's reads and writes with XOR in place of its arithmetic, on the
+// combine's row map or on rows in address order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -72,6 +74,42 @@ __global__ void __launch_bounds__(64) probe_gather_kernel(const int32_t *dst_row
     sink[(size_t)gw * 64 + lane] = acc;
 }
 
+// the combine's bytes without its arithmetic: one wave per (token, 2 KB slice) as above, the
+// token's K rows folded with XOR and the fold stored (non-temporal) to out row t.  GATHER: rows
+// dst_row[t, j] (skipped when negative), the combine's pattern; otherwise rows t K + j, every
+// row read once in address order and the outputs written in address order.
+template <int KMAX, bool GATHER>
+__global__ void __launch_bounds__(64) probe_reduce_kernel(const int32_t *dst_row, int K, int row_bytes,
+                                                          const unsigned char *buf, int nslice, unsigned char *out) {
+  const int lane = threadIdx.x;
+  const int gw = blockIdx.x;
+  const int t = gw / nslice, sl = gw - t * nslice;
+  const int nch = row_bytes / 16;
+  const int c0 = 128 * sl + lane, c1 = c0 + 64;
+  int myrow = -1;
+  if (lane < K) myrow = GATHER ? dst_row[(size_t)t * K + lane] : t * K + lane;
+  u32x4 v[2 * KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const int r = __builtin_amdgcn_readlane(myrow, j);
+    v[2 * j] = v[2 * j + 1] = u32x4{0u, 0u, 0u, 0u};
+    if (j < K && r >= 0) {
+      const u32x4 *row = (const u32x4 *)(buf + (size_t)r * row_bytes);
+      if (c0 < nch) v[2 * j] = __builtin_nontemporal_load(row + c0);
+      if (c1 < nch) v[2 * j + 1] = __builtin_nontemporal_load(row + c1);
+    }
+  }
+  u32x4 a0 = u32x4{0u, 0u, 0u, 0u}, a1 = a0;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    a0 ^= v[2 * j];
+    a1 ^= v[2 * j + 1];
+  }
+  u32x4 *o = (u32x4 *)(out + (size_t)t * row_bytes);
+  if (c0 < nch) __builtin_nontemporal_store(a0, o + c0);
+  if (c1 < nch) __builtin_nontemporal_store(a1, o + c1);
+}
+
 int block_for(int row_bytes) { return 64 * ((row_bytes / 16 + 63) / 64); }
 
 }  // namespace
@@ -123,6 +161,37 @@ int moe_probe_gather_read(const int32_t *dst_row, int T, int K, int row_bytes, c
   else
     hipLaunchKernelGGL(probe_gather_kernel<16>, grid, dim3(64), 0, (hipStream_t)stream, dst_row, K, row_bytes,
                        (const unsigned char *)buf, nslice, (u32x4 *)sink);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// The combine's reads and writes without its arithmetic (probe_reduce_kernel): out row t (T rows
+// of row_bytes) = XOR of the token's K rows of buf.  gather != 0: rows dst_row[t, j] (negative
+// entries skipped; buf holds max(dst_row) + 1 rows); gather == 0: rows t K + j (buf holds T K
+// rows, dst_row unused).  row_bytes a multiple of 16, at most 16384; K at most 16; buf and out
+// 16-byte aligned.  Returns 0, or -1 for bad arguments, -5 when the launch fails.
+int moe_probe_reduce(const int32_t *dst_row, int T, int K, int row_bytes, const void *buf, void *out, int gather,
+                     void *stream) {
+  if (T < 0 || K <= 0 || K > 16 || row_bytes <= 0 || row_bytes % 16 || row_bytes > 16384 || !buf || !out ||
+      (T > 0 && gather && !dst_row) || (int64_t)T * K > 0x7fffffff)
+    return -1;
+  if ((((uintptr_t)buf | (uintptr_t)out) & 15u) != 0) return -1;
+  if (T == 0) return 0;
+  const int nslice = (row_bytes / 16 + 127) / 128;
+  const dim3 grid((unsigned)((int64_t)T * nslice));
+  const hipStream_t st = (hipStream_t)stream;
+  const unsigned char *b = (const unsigned char *)buf;
+  unsigned char *o = (unsigned char *)out;
+  if (K <= 8) {
+    if (gather)
+      hipLaunchKernelGGL((probe_reduce_kernel<8, true>), grid, dim3(64), 0, st, dst_row, K, row_bytes, b, nslice, o);
+    else
+      hipLaunchKernelGGL((probe_reduce_kernel<8, false>), grid, dim3(64), 0, st, dst_row, K, row_bytes, b, nslice, o);
+  } else {
+    if (gather)
+      hipLaunchKernelGGL((probe_reduce_kernel<16, true>), grid, dim3(64), 0, st, dst_row, K, row_bytes, b, nslice, o);
+    else
+      hipLaunchKernelGGL((probe_reduce_kernel<16, false>), grid, dim3(64), 0, st, dst_row, K, row_bytes, b, nslice, o);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
