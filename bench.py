@@ -927,6 +927,7 @@ def main():
                 T=cfg["T"], H=cfg["H"], k=cfg["k"], E=cfg["E"], P=cfg["P"], zero_copy_const=cfg["zero_copy_const"],
                 quant_mode=cfg["quant_mode"], rows_N=cfg["rows_N"], rotating_input_sets=cfg["rotating_input_sets"],
                 us_per_layer=sub["us_per_layer"], value_GBps=sub["value"], pct_of_peak=sub["pct_of_peak"],
+                three_call_us_per_layer=sub["three_call_step"]["us_per_layer"],
                 layout_us=k["layout"]["kernel_us"], layout_launches=k["layout"]["launches"],
                 dispatch=dict((f, k["dispatch"][f]) for f in ("kernel_us", "comm_bytes", "hbm_bytes", "comm_GBps",
                                                                 "comm_pct_of_peak", "hbm_pct_of_peak", "payload")),

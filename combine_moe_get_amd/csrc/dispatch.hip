@@ -79,9 +79,10 @@ __device__ __forceinline__ void dispatch_copy_item(const DispatchArgs &a, int ns
 // items: T * nslice (token, slice) pairs.  LOOP: a grid smaller than that (a capped launch) walks
 // them with a grid stride; otherwise one workgroup per item (the loop costs registers: 12 -> 18).
 // NT: non-temporal stores, used when the token rows were just read ahead into the Infinity Cache
-// (moe_layout_dispatch): there the copy measured faster with them (workload T=4096, H=7168, top-8,
-// Zipf: 194.9 against 196.3 us per layer with sc1 stores; at T=8192, H=4096: 224.7 against 228.0),
-// while without the read-ahead sc1 stores are faster (101.5 against 104 us for the copy alone).
+// (moe_layout_dispatch).  With the read-ahead, sc1 stores made the layer slower (T=4096, H=7168,
+// top-8, Zipf: 202.8 against 196.4 us per layer without read-ahead), non-temporal ones did not
+// (194.4-195.4); without the read-ahead sc1 stores are the faster (101.5 against 104 us for the
+// copy alone).
 template <bool LOOP, bool NT>
 __global__ void __launch_bounds__(64) dispatch_copy_kernel(DispatchArgs a, int nslice, int items) {
   if constexpr (LOOP) {

@@ -227,7 +227,10 @@ int moe_dispatch_capped(const moe_get_shape_t *shape, int32_t max_workgroups, in
  * rows itself and dispatches a share of the chunk's tokens -- which saves the
  * launches between layout and dispatch on the decode-sized batches the
  * low-latency kernels target; larger worlds run the layout kernels, then the
- * dispatch kernel.  Workspace as for moe_get_layout. */
+ * dispatch kernel, and the layout kernels also read x (T * H * 2 bytes, loads
+ * only) so that the dispatch finds its rows in the GPU's caches.  x is read,
+ * never written; it must not be written by other work while the call runs, as
+ * for moe_dispatch.  Workspace as for moe_get_layout. */
 int moe_layout_dispatch(const moe_get_shape_t *shape, int64_t rank_stride, int32_t quant_mode,
                         const int32_t *topk_idx, const uint8_t *x_active_mask, const uint16_t *x,
                         const float *x_smooth_scale, int32_t smooth_rows, const float *topk_weights,

@@ -115,7 +115,7 @@ def test_fused_named_workloads(cid, T, P, launches):
 
 
 @pytest.mark.parametrize("case", ["wide_E", "max_slots", "big_chunk", "ragged_chunks", "big_world", "ragged_H",
-                                  "max_H", "empty", "per_expert_share"])
+                                  "max_H", "empty", "per_expert_share", "ragged_read_ahead"])
 def test_fused_edge_cases(case):
     r = workloads.rng_for(11, 77, 0)
     launches = 1
@@ -129,6 +129,9 @@ def test_fused_edge_cases(case):
         T, H, K, E, P = 200, 512, 6, 40, 2
     elif case == "big_world":  # T * K above the single-launch bound: two layout launches + dispatch
         T, H, K, E, P = 1024, 1024, 16, 64, 2
+        launches = 3
+    elif case == "ragged_read_ahead":  # two layout launches whose read-ahead splits T H 2 bytes unevenly
+        T, H, K, E, P = 1023, 1032, 16, 66, 3  # (T H 2 = 16 mod 32: halves of 1055728 and 1055744 bytes)
         launches = 3
     elif case == "ragged_H":
         T, H, K, E, P = 96, 520, 4, 32, 4
