@@ -27,9 +27,10 @@
 // copy reads through a buffer resource, row_load).
 // Receive rows are written once and read by a later kernel: the int8 codes are
 // stored non-temporally, the bf16 copies of dispatch_copy_kernel with the sc1
-// policy (row_store_sc1), whichever measured faster for each (the single-launch
-// layout + dispatch kernel, for batches of at most 8192 slots, keeps
-// non-temporal stores for both).
+// policy (row_store_sc1), whichever measured faster for each; after the
+// read-ahead of moe_layout_dispatch the bf16 copies are stored non-temporally
+// too (the NT form), and the single-launch layout + dispatch kernel, for
+// batches of at most 8192 slots, keeps non-temporal stores for both.
 #include "dispatch_dev.hpp"
 
 namespace moe {
