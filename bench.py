@@ -546,7 +546,7 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False,
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    for g in gsets:  # arguments checked and marshalled once; a step is three bare C calls
+    for g in gsets:  # arguments checked and marshalled once; a step is two bare C calls
         g["c_lay"] = mg.prepare_layout(shape, g["topk"], g["mask"], out=g["lay"], workspace=g["ws"], rank_stride=A)
         g["c_dis"] = mg.prepare_dispatch(shape, qm, g["x"], g["lay"].dst_row, g["smooth"], None, g["topk"],
                                          g["ex"], g["ds"], rows=cap)
