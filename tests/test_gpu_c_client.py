@@ -14,7 +14,7 @@ from combine_moe_get_amd.workloads import expert_out_normal, fuzz_world, make_in
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
-from _gpu import ATOL, RTOL, LAYOUT_KEYS, assert_combine_close  # noqa: E402,F401
+from _gpu import LAYOUT_KEYS, assert_combine_close  # noqa: E402
 from c_client import build as cbuild  # noqa: E402
 
 

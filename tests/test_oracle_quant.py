@@ -7,7 +7,6 @@ rational evaluation in which each binary32 operation is rounded once
 scale, a wrong rounding mode or a reassociated product would break.
 """
 import json
-import math
 import os
 from fractions import Fraction
 
