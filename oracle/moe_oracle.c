@@ -201,10 +201,10 @@ int orc_layout_ex(const orc_shape_t *s, int64_t rank_stride, const int32_t *topk
           int64_t placed = row;
           if (id != e || slot_class(s, mask, t, id) != SLOT_ROUTED) continue;
           if (rank_stride > 0) {
-            int r = e / L;
-            int64_t local = row - rank_offsets[r];
+            int owner = e / L;
+            int64_t local = row - rank_offsets[owner];
             placed = -1;
-            if (local < rank_stride) placed = (int64_t)r * rank_stride + local;
+            if (local < rank_stride) placed = (int64_t)owner * rank_stride + local;
             else bad |= 2;
           }
           ++row;
