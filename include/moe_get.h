@@ -200,7 +200,8 @@ size_t moe_get_noalloc_scratch_bytes(void);
  * int8 codes: x_fp32 = fp32(x) * scales rounded to binary32; dyn = 127 / amax
  * correctly rounded; q = round-half-even(x_fp32 * dyn) saturated to
  * [-127, 127] (a NaN product, 0 * inf, gives 0); amax == 0 gives q = 0 and
- * scale 0. */
+ * scale 0.  Launches one kernel; with quant_mode MOE_QUANT_STATIC_INT8, two (a
+ * sequential read of x ahead of the dispatch kernel). */
 int moe_dispatch(const moe_get_shape_t *shape, int32_t quant_mode, const uint16_t *x,
                  const float *x_smooth_scale, int32_t smooth_rows, const float *topk_weights,
                  const int32_t *topk_idx, const int32_t *dst_row, void *expand_x,
