@@ -835,9 +835,9 @@ hipError_t launch_layout_dispatch(const LayoutArgs &a, const DispatchArgs &d, in
   // of theirs read the dispatch's token rows ahead into the Infinity Cache (results unchanged).
   // Measured per layer (layout + dispatch + combine, ten rotating input sets, one process, the same
   // builds alternated): T=4096, H=7168, top-8, int8 157.0 -> 152.0 us; T=16384 masked int8 570.4 ->
-  // 560.3 us; bf16 rows (the copy's stores then non-temporal) within 1 us of no read-ahead
-  // (196.0 -> 195.1 us at T=4096, 223.2 -> 222.3 us at T=8192, H=4096).  128 extra workgroups per
-  // kernel measured best of 64, 128 and 256 (64: slower than none).
+  // 560.3 us; bf16 rows (the copy's stores then non-temporal) about 1% (196.2 -> 194.6 us at T=4096,
+  // 227.4 -> 224.9 us at T=8192, H=4096; 8 alternated repetitions).  128 extra workgroups per kernel
+  // measured best of 64, 128 and 256 (64: slower than none).
   LayoutArgs b = a;
   const bool ahead = d.x && a.T > 0;
   if (ahead) {
