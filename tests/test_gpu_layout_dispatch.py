@@ -102,6 +102,39 @@ def test_fused_fuzz_worlds(seed):
                 fz["mask"], fz["x"], fz["topk_weights"], qm, smooth, stride=stride, label=f"fuzz seed {seed}")
 
 
+def _two_launch_world(seed):
+    # a random world above the single-launch bound (T K > 8192 slots): the layout kernels, whose
+    # extra workgroups read the token rows ahead, then the dispatch kernel
+    r = np.random.default_rng(4000 + seed)
+    P = int(r.choice([2, 3, 4, 8, 16]))
+    L = int(r.integers(2, 17))
+    Z, C, Kc = (int(v) for v in r.integers(0, 3, 3))
+    K = int(r.integers(8, min(16, P * L + Z + C + Kc) + 1))
+    if P * 512 * K <= 8192:  # chunks of at most 512 tokens could not pass the bound
+        P = 4
+    E = P * L
+    bs_min = -(-8193 // (P * K))
+    BS = min(512, bs_min + int(r.integers(0, 100)))
+    H = 8 * int(r.integers(1, 65))
+    fz = workloads.fuzz_world(seed, T=P * BS, H=H, K=K, E=E, P=P, Z=Z, C=C, Kc=Kc,
+                              p_bad=0.02 if seed % 5 == 4 else 0.0)
+    return fz
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_fused_fuzz_worlds_two_launch(seed):
+    fz = _two_launch_world(seed)
+    _, qm, smooth, stride = _fuzz_args(seed)
+    if smooth is not None and smooth.ndim == 2:  # [E, H] rows for this world's E and H
+        smooth = np.ascontiguousarray(workloads.rng_for(seed, 5, 0).uniform(0.5, 1.5, (fz["E"], fz["H"])),
+                                      np.float32)
+    elif smooth is not None:
+        smooth = fz["smooth"]
+    check_fused(fz["T"], fz["H"], fz["K"], fz["E"], fz["P"], fz["Z"], fz["C"], fz["Kc"], fz["topk_idx"],
+                fz["mask"], fz["x"], fz["topk_weights"], qm, smooth, stride=stride,
+                label=f"two-launch fuzz seed {seed}", expect_launches=3)
+
+
 @pytest.mark.parametrize("cid,T,P,launches", [(2, 128, 1, 1), (2, 1024, None, 1), (2, None, None, 3),
                                               (3, 1024, None, 1), (3, None, None, 3), (4, 512, None, 1),
                                               (5, 1024, None, 1),
