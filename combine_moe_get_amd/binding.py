@@ -457,7 +457,8 @@ def layout_dispatch(shape, quant_mode, x, topk_idx, x_active_mask=None, x_smooth
                     out=None, expand_x=None, dynamic_scales=None, expand_weights=None, workspace=None,
                     stream=None, rank_stride=0):
     """moe_layout_dispatch: layout and dispatch in one call (one kernel for T * K <= 8192
-    slots).  Returns (Layout, expand_x, dynamic_scales or None, expand_weights or None),
-    identical to layout() followed by dispatch()."""
+    slots; above that the layout kernels, which also read x ahead into the GPU's caches, then
+    the dispatch kernel).  Returns (Layout, expand_x, dynamic_scales or None, expand_weights or
+    None), identical to layout() followed by dispatch()."""
     return prepare_layout_dispatch(shape, quant_mode, x, topk_idx, x_active_mask, x_smooth_scale, topk_weights,
                                    out, expand_x, dynamic_scales, expand_weights, workspace, rank_stride)(stream)
