@@ -302,7 +302,7 @@ def test_rank_window_below_capacity_is_refused():
 # ---- prepared calls and graph capture ---------------------------------------------------
 
 
-def _prepared_world(cid=2, T=1024, seed=0):
+def _prepared_world(cid=2, T=1024, seed=0, qm=2):
     inp = workloads.make_inputs(cid, seed=seed, T=T)
     c = inp["cfg"]
     shape, osh = G.shapes(c["T"], c["H"], c["K"], c["E"], c["P"], c["Z"], c["C"], c["Kc"], c["num_max"])
@@ -312,11 +312,11 @@ def _prepared_world(cid=2, T=1024, seed=0):
     ws = mg.alloc_workspace(shape, G.DEV)
     cap = c["T"] * c["K"]
     ex = torch.empty((cap, c["H"]), dtype=torch.int8, device=G.DEV)
-    ds = torch.empty(cap, dtype=torch.float32, device=G.DEV)
+    ds = torch.empty(cap, dtype=torch.float32, device=G.DEV) if qm == 2 else None
     y = G.dev(workloads.expert_out_normal(cap, c["H"], seed=seed))
     out = torch.empty((c["T"], c["H"]), dtype=torch.bfloat16, device=G.DEV)
     calls = (mg.prepare_layout(shape, d["topk"], None, out=lay, workspace=ws),
-             mg.prepare_dispatch(shape, 2, d["x"], lay.dst_row, d["s"], None, d["topk"], ex, ds),
+             mg.prepare_dispatch(shape, qm, d["x"], lay.dst_row, d["s"], None, d["topk"], ex, ds),
              mg.prepare_combine(shape, y, d["topk"], d["w"], lay.dst_row, out=out))
     return inp, shape, osh, lay, ex, ds, y, out, calls
 
@@ -335,13 +335,17 @@ def test_prepared_calls_match_the_oracle():
     G.assert_combine_close(G.host_bf16(out), co)
 
 
-def test_graph_replays_match_eager():
+@pytest.mark.parametrize("qm", [2, 1])  # static codes: moe_dispatch launches its read-ahead kernel first
+def test_graph_replays_match_eager(qm):
     # the whole path captured once and replayed several times, with eager work and
     # synchronizations between replays; every replay must equal the eager result bit for bit
-    inp, shape, osh, lay, ex, ds, y, out, calls = _prepared_world(seed=4)
+    inp, shape, osh, lay, ex, ds, y, out, calls = _prepared_world(seed=4, qm=qm)
+    print(f"[graph] quant_mode={qm}", flush=True)
     for c in calls:
         c()
     torch.cuda.synchronize()
+    if ds is None:
+        ds = torch.zeros(1, device=G.DEV)
     ref = (lay.dst_row.clone(), lay.src_info.clone(), ex.clone(), ds.clone(), out.clone())
     gr = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gr):
