@@ -744,7 +744,7 @@ def measure(args, mg, workloads, dev, tokens=None, ranks=None, copy_probe=False,
     # moe_combine; the dispatch then reads the token rows from HBM)
     k_ld = kernel_avg_ms(lambda g: g["c_ld"](stream))
     three_call = dict(us_per_layer=round(three_ms * 1e3, 2), layout_dispatch_call_us=round(k_ld * 1e3, 2),
-                      layout_dispatch_launches=mg.layout_dispatch_launches(shape),
+                      layout_dispatch_launches=mg.layout_dispatch_launches(shape, qm),
                       what="us_per_layer: the step as moe_get_layout + moe_dispatch + moe_combine (timed like the "
                            "headline step); layout_dispatch_call_us: moe_layout_dispatch back to back")
 

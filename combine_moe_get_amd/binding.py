@@ -110,7 +110,7 @@ def lib():
         L.moe_get_layout_launches.restype = ctypes.c_int
         L.moe_layout_dispatch.argtypes = [SP, I64, I32, V, V, V, V, I32, V] + [V] * 12 + [V, V, SZ, V]
         L.moe_layout_dispatch.restype = ctypes.c_int
-        L.moe_layout_dispatch_launches.argtypes = [SP]
+        L.moe_layout_dispatch_launches.argtypes = [SP, ctypes.c_int32]
         L.moe_layout_dispatch_launches.restype = ctypes.c_int
         L.moe_dispatch.argtypes = [SP, I32, V, V, I32, V, V, V, V, V, V, V]
         L.moe_dispatch.restype = ctypes.c_int
@@ -157,9 +157,10 @@ def layout_launches(shape):
     return n
 
 
-def layout_dispatch_launches(shape):
-    """Kernel launches moe_layout_dispatch makes for this shape (moe_layout_dispatch_launches)."""
-    n = lib().moe_layout_dispatch_launches(ctypes.byref(shape))
+def layout_dispatch_launches(shape, quant_mode):
+    """Kernel launches moe_layout_dispatch makes for this shape and quant mode
+    (moe_layout_dispatch_launches)."""
+    n = lib().moe_layout_dispatch_launches(ctypes.byref(shape), int(quant_mode))
     if n < 0:
         raise MoeGetError("moe_layout_dispatch_launches", n)
     return n

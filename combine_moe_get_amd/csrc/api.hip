@@ -371,10 +371,12 @@ int moe_layout_dispatch(const moe_get_shape_t *shape, int64_t rank_stride, int32
                                                                                                   : MOE_ERR_HIP;
 }
 
-int moe_layout_dispatch_launches(const moe_get_shape_t *shape) {
+int moe_layout_dispatch_launches(const moe_get_shape_t *shape, int32_t quant_mode) {
   const int st = check_shape(shape);
   if (st != MOE_OK) return st;
-  return layout_dispatch_launch_count(layout_sizes(shape));
+  if (quant_mode < 0 || quant_mode > 2) return MOE_ERR_ARG;
+  return layout_dispatch_launch_count(layout_sizes(shape), quant_mode,
+                                      (int64_t)shape->num_tokens * shape->hidden * 2);
 }
 
 int moe_combine(const moe_get_shape_t *shape, const uint16_t *expert_out,

@@ -20,8 +20,8 @@
 //  - int8 with per-expert scales: one workgroup per token (dynamic) or per
 //    (token, expert-id parity) (static), the copies quantized one at a time (see
 //    dispatch_quant_expert_kernel).
-// Static codes from moe_dispatch are preceded by a sequential read-ahead of the token
-// rows (dispatch_read_ahead_kernel, see launch_dispatch).
+// Static codes from moe_dispatch on large batches are preceded by a sequential read-ahead
+// of the token rows (dispatch_read_ahead_kernel, see launch_dispatch).
 // Every kernel also has a looping form for moe_dispatch_capped: a grid of at most
 // max_workgroups workgroups walks the same work items with a grid stride (the per-item
 // code is shared, so the results are identical).
@@ -275,20 +275,33 @@ static void launch_dispatch_grid(const DispatchArgs &a, int quant_mode, bool per
 // The static kernels have no amax barrier, and their row reads from HBM interleave with their
 // stores and scale reads; read in one sequential pass first, moe_dispatch measured (T=4096,
 // H=7168, top-8, ten rotating sets, same process) 108.3 -> 98.1 us with [E, H] scales and
-// 61.1 -> 57.9 us with one [H] vector.  The dynamic kernels lost with it (120.5 -> 125.4 and
-// 58.7 -> 59.5 us), so they read their rows themselves.  256 workgroups measured as 1024.
+// 61.1 -> 57.9 us with one [H] vector, at T=2048 58.0 -> 53.6 and 32.3 -> 30.1 us; at T <= 1024
+// (x <= 14.7 MB) the extra launch cost more than it saved (12.4 -> 16.0 us at T=1024, [H]), so
+// the pass runs only for x of at least 24 MiB.  The dynamic kernels lost with it (120.5 -> 125.4
+// and 58.7 -> 59.5 us at T=4096), so they read their rows themselves.  256 workgroups measured
+// as 1024.
 static constexpr int kPrepassWorkgroups = 256;
+static constexpr int64_t kPrepassMinBytes = (int64_t)24 << 20;
 
 __global__ void __launch_bounds__(1024) dispatch_read_ahead_kernel(const void *x, int64_t bytes) {
   read_ahead(x, 0, bytes, blockIdx.x, gridDim.x);
 }
 
+static bool use_prepass(int quant_mode, int max_wg, bool rows_cached, int64_t x_bytes) {
+  return quant_mode == 1 && !rows_cached && max_wg == 0 && x_bytes >= kPrepassMinBytes;
+}
+
+int dispatch_launch_count(int quant_mode, int max_wg, bool rows_cached, int64_t x_bytes) {
+  return use_prepass(quant_mode, max_wg, rows_cached, x_bytes) ? 2 : 1;
+}
+
 hipError_t launch_dispatch(const DispatchArgs &a, int quant_mode, bool per_expert, hipStream_t stream,
                            int max_wg, bool rows_cached) {
   if (a.T == 0) return hipSuccess;
-  if (quant_mode == 1 && !rows_cached && max_wg == 0)
+  const int64_t x_bytes = (int64_t)a.T * a.H * 2;
+  if (use_prepass(quant_mode, max_wg, rows_cached, x_bytes))
     hipLaunchKernelGGL(dispatch_read_ahead_kernel, dim3(kPrepassWorkgroups), dim3(1024), 0, stream,
-                       (const void *)a.x, (int64_t)a.T * a.H * 2);
+                       (const void *)a.x, x_bytes);
   if (max_wg > 0)
     launch_dispatch_grid<true>(a, quant_mode, per_expert, stream, max_wg, rows_cached);
   else

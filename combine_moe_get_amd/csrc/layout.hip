@@ -41,8 +41,14 @@ namespace moe {
 int layout_waves(int E) { return E <= 1024 ? 16 : 8; }
 
 // the single-launch layout re-reads every token's ids in each of the P workgroups; that pass is
-// latency-bound, so it only pays while it is short (one launch saved)
+// latency-bound, so it only pays while it is short (one launch saved).  With an int8 dispatch in
+// the same kernel the bound is lower: per layer (layout + dispatch + combine, T=256..1024, H=7168,
+// top-8, dynamic codes) the single kernel measured 18.4 against 19.0 us at 2048 slots, but 28.3
+// against 27.4 at 4096 and 49.1 against 46.0-46.4 at 8192 (P = 4..32); with bf16 rows it stays
+// ahead up to 8192 slots (29.8 against 32.2, 54.3 against 57.2 us at H=7168; 20.8 against 23.2,
+// 34.4 against 37.8 at H=4096 with special experts).
 static constexpr int64_t kFusedMaxSlots = 8192;  // measured: faster below ~10K slots, slower above
+static constexpr int64_t kFusedInt8MaxSlots = 2048;  // the single kernel with an int8 dispatch
 static constexpr size_t kMaxLds = 160 * 1024;  // gfx950 LDS per workgroup
 static constexpr int kSpecPerBlock = 8;        // special-id totals one scan workgroup sums from its prefetch
 static constexpr int kReadAheadWorkgroups = 128;  // per layout kernel, see launch_layout_dispatch
@@ -731,16 +737,20 @@ static int fused_tpw(const LayoutArgs &a, bool dispatch) {
 }
 
 // single launch while each workgroup's pass over every token stays small
-static bool use_fused(const LayoutArgs &a, bool rows) {
+// (rows: with the dispatch of quant_mode quant in the same kernel)
+static bool use_fused(const LayoutArgs &a, bool rows, int quant = 0) {
   const size_t flds = layout_fused_lds_bytes(layout_waves(a.E), a.E, a.NS, a.Epad, a.K, a.P, fused_tpw(a, rows), rows);
-  return (int64_t)a.T * a.K <= kFusedMaxSlots && flds <= kMaxLds;
+  const int64_t max_slots = rows && quant != 0 ? kFusedInt8MaxSlots : kFusedMaxSlots;
+  return (int64_t)a.T * a.K <= max_slots && flds <= kMaxLds;
 }
 
 int layout_launch_count(const LayoutArgs &a) { return use_fused(a, false) ? 1 : 2; }
 
-int layout_dispatch_launch_count(const LayoutArgs &a) {
-  if (use_fused(a, true)) return 1;
-  return layout_launch_count(a) + (a.T > 0 ? 1 : 0);
+int layout_dispatch_launch_count(const LayoutArgs &a, int quant_mode, int64_t x_bytes) {
+  if (use_fused(a, true, quant_mode)) return 1;
+  if (a.T == 0) return layout_launch_count(a);
+  const bool ahead = !use_fused(a, false);  // the two layout kernels read the rows ahead
+  return layout_launch_count(a) + dispatch_launch_count(quant_mode, 0, ahead, x_bytes);
 }
 
 template <int W, int DM, bool PE>
@@ -827,7 +837,7 @@ hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {
 
 hipError_t launch_layout_dispatch(const LayoutArgs &a, const DispatchArgs &d, int quant_mode, bool per_expert,
                                   hipStream_t stream) {
-  if (use_fused(a, true)) {
+  if (use_fused(a, true, quant_mode)) {
     return layout_waves(a.E) == 16 ? launch_fused_mode<16>(a, d, quant_mode, per_expert, stream)
                                    : launch_fused_mode<8>(a, d, quant_mode, per_expert, stream);
   }
@@ -838,8 +848,10 @@ hipError_t launch_layout_dispatch(const LayoutArgs &a, const DispatchArgs &d, in
   // 560.3 us; bf16 rows (the copy's stores then non-temporal) about 1% (196.2 -> 194.6 us at T=4096,
   // 227.4 -> 224.9 us at T=8192, H=4096; 8 alternated repetitions).  128 extra workgroups per kernel
   // measured best of 64, 128 and 256 (64: slower than none).
+  // (only the two-kernel layout carries the read-ahead workgroups; a world small enough for the
+  // single-kernel layout, dispatched in a second kernel, reads its rows in the dispatch)
   LayoutArgs b = a;
-  const bool ahead = d.x && a.T > 0;
+  const bool ahead = d.x && a.T > 0 && !use_fused(a, false);
   if (ahead) {
     b.pf = d.x;
     b.pf_bytes = (int64_t)a.T * d.H * 2;

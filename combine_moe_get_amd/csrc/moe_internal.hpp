@@ -204,7 +204,9 @@ int layout_launch_count(const LayoutArgs &a);  // kernels launch_layout runs for
 // layout and dispatch of the same call (one kernel for small worlds, else the two paths in turn)
 hipError_t launch_layout_dispatch(const LayoutArgs &a, const DispatchArgs &d, int quant_mode, bool per_expert,
                                   hipStream_t stream);
-int layout_dispatch_launch_count(const LayoutArgs &a);
+int layout_dispatch_launch_count(const LayoutArgs &a, int quant_mode, int64_t x_bytes);
+// kernels launch_dispatch runs (uncapped when max_wg == 0) for T > 0
+int dispatch_launch_count(int quant_mode, int max_wg, bool rows_cached, int64_t x_bytes);
 // max_wg > 0: launch at most that many workgroups, each walking several work items (a capped
 // grid, which leaves the rest of the GPU to kernels running beside it); 0: one per item.
 // rows_cached: the token rows were just read ahead into the caches (the bf16 copy then stores

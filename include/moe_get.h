@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOE_GET_ABI_VERSION 1
+#define MOE_GET_ABI_VERSION 2
 
 /* Sizes of one call.  Constraints section of "low_latency_dispatch":
  * 0 < K <= 16 and K <= Etot; BS <= 512; E a multiple of P; L * P <= 2048;
@@ -200,8 +200,9 @@ size_t moe_get_noalloc_scratch_bytes(void);
  * int8 codes: x_fp32 = fp32(x) * scales rounded to binary32; dyn = 127 / amax
  * correctly rounded; q = round-half-even(x_fp32 * dyn) saturated to
  * [-127, 127] (a NaN product, 0 * inf, gives 0); amax == 0 gives q = 0 and
- * scale 0.  Launches one kernel; with quant_mode MOE_QUANT_STATIC_INT8, two (a
- * sequential read of x ahead of the dispatch kernel). */
+ * scale 0.  Launches one kernel; with quant_mode MOE_QUANT_STATIC_INT8 and x of
+ * at least 24 MiB (T * H * 2 bytes), two (a sequential read of x ahead of the
+ * dispatch kernel). */
 int moe_dispatch(const moe_get_shape_t *shape, int32_t quant_mode, const uint16_t *x,
                  const float *x_smooth_scale, int32_t smooth_rows, const float *topk_weights,
                  const int32_t *topk_idx, const int32_t *dst_row, void *expand_x,
@@ -224,12 +225,13 @@ int moe_dispatch_capped(const moe_get_shape_t *shape, int32_t max_workgroups, in
  * identical, bit for bit, to moe_get_layout_ex(shape, rank_stride, ...)
  * followed by moe_dispatch(shape, quant_mode, ...) with the same arguments;
  * argument rules and errors are the union of theirs.  Small worlds (T * K <=
- * 8192 slots) run as a single kernel -- every workgroup derives its chunk's
- * rows itself and dispatches a share of the chunk's tokens -- which saves the
- * launches between layout and dispatch on the decode-sized batches the
- * low-latency kernels target; larger worlds run the layout kernels, then the
- * dispatch kernel, and the layout kernels also read x (T * H * 2 bytes, loads
- * only) so that the dispatch finds its rows in the GPU's caches.  x is read,
+ * 8192 slots with bf16 rows, <= 2048 with int8 codes) run as a single kernel --
+ * every workgroup derives its chunk's rows itself and dispatches a share of the
+ * chunk's tokens -- which saves the launches between layout and dispatch on the
+ * decode-sized batches the low-latency kernels target; larger worlds run the
+ * layout (one kernel up to 8192 slots, else two, which also read x, T * H * 2
+ * bytes, loads only, so that the dispatch finds its rows in the GPU's caches),
+ * then the dispatch (see moe_dispatch).  x is read,
  * never written; it must not be written by other work while the call runs, as
  * for moe_dispatch.  Workspace as for moe_get_layout. */
 int moe_layout_dispatch(const moe_get_shape_t *shape, int64_t rank_stride, int32_t quant_mode,
@@ -241,10 +243,11 @@ int moe_layout_dispatch(const moe_get_shape_t *shape, int64_t rank_stride, int32
                         float *dynamic_scales, float *expand_weights, uint32_t *status_dev, void *workspace,
                         size_t workspace_bytes, void *stream);
 
-/* Kernel launches one moe_layout_dispatch call makes for this shape (1 when
- * the layout is a single launch, else the layout's launches plus one); a negative
- * MOE_ERR_* for an invalid shape. */
-int moe_layout_dispatch_launches(const moe_get_shape_t *shape);
+/* Kernel launches one moe_layout_dispatch call makes for this shape and
+ * quant_mode (1 when layout and dispatch run as a single kernel, else the
+ * layout's launches plus the dispatch's); a negative MOE_ERR_* for an invalid
+ * shape, MOE_ERR_ARG for a quant_mode outside 0..2. */
+int moe_layout_dispatch_launches(const moe_get_shape_t *shape, int32_t quant_mode);
 
 /* Combine: out[t] = bf16( sum_j w[t,j] * Moe_j(t) ), fp32 accumulation in
  * slot order j = 0..K-1, where Moe_j is

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert mg.abi_version() == 1
+    assert mg.abi_version() == 2
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert mg.status_string(code) and mg.status_string(code) != "unknown status"
     assert mg.status_string(42) == "unknown status"

@@ -112,7 +112,7 @@ def test_layout_dispatch_writes_only_the_layout_rows(T, qm, stride):
     shape, osh = G.shapes(T, H, K, E, P)
     A = mg.rank_capacity(shape) if stride == "min" else 0
     cap = P * A if A else T * K
-    print(f"[guard] layout_dispatch T={T} qm={qm} A={A} launches={mg.layout_dispatch_launches(shape)}", flush=True)
+    print(f"[guard] layout_dispatch T={T} qm={qm} A={A} launches={mg.layout_dispatch_launches(shape, qm)}", flush=True)
     full, (ex, ds, ew, src) = _canary_outputs(cap, H, qm)
     lay = mg.alloc_layout(shape, G.DEV, A)._replace(src_info=src)
     mg.layout_dispatch(shape, qm, G.dev(x), G.dev(topk), G.dev(m), G.dev(s) if qm else None, G.dev(w),

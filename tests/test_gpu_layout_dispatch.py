@@ -39,7 +39,7 @@ def check_fused(T, H, K, E, P, Z, C, Kc, topk, mask, x, w, qm, smooth, num_max=0
                 expect_launches=None):
     shape = mg.make_shape(T, H, K, E, P, Z, C, Kc, num_max)
     A = mg.rank_capacity(shape) if stride == "min" else int(stride)
-    n_launch = mg.layout_dispatch_launches(shape)
+    n_launch = mg.layout_dispatch_launches(shape, qm)
     print(f"[fused] {label} T={T} H={H} K={K} E={E} P={P} Z={Z} C={C} Kc={Kc} qm={qm} "
           f"smooth_rows={G.smooth_rows_of(smooth, H)} mask={mask is not None} stride={A} launches={n_launch}",
           flush=True)
@@ -135,9 +135,12 @@ def test_fused_fuzz_worlds_two_launch(seed):
                 label=f"two-launch fuzz seed {seed}", expect_launches=3)
 
 
-@pytest.mark.parametrize("cid,T,P,launches", [(2, 128, 1, 1), (2, 1024, None, 1), (2, None, None, 3),
+# launches: 1 while layout and dispatch share one kernel (T K <= 8192 slots for bf16 rows, <= 2048 for
+# int8 codes); the single-kernel layout then the dispatch kernel (2) up to 8192 slots; above that the
+# two layout kernels, with the read-ahead, then the dispatch (3)
+@pytest.mark.parametrize("cid,T,P,launches", [(2, 128, 1, 1), (2, 1024, None, 2), (2, None, None, 3),
                                               (3, 1024, None, 1), (3, None, None, 3), (4, 512, None, 1),
-                                              (5, 1024, None, 1),
+                                              (5, 1024, None, 2),
                                               (1, None, None, 1)])
 def test_fused_named_workloads(cid, T, P, launches):
     inp = workloads.make_inputs(cid, seed=3, T=T, P=P)
@@ -147,8 +150,8 @@ def test_fused_named_workloads(cid, T, P, launches):
                 label=f"workload {cid} ({c['name']})", expect_launches=launches)
 
 
-@pytest.mark.parametrize("case", ["wide_E", "max_slots", "big_chunk", "ragged_chunks", "big_world", "ragged_H",
-                                  "max_H", "empty", "per_expert_share", "ragged_read_ahead"])
+@pytest.mark.parametrize("case", ["wide_E", "max_slots", "int8_max_slots", "big_chunk", "ragged_chunks", "big_world",
+                                  "ragged_H", "max_H", "empty", "per_expert_share", "ragged_read_ahead"])
 def test_fused_edge_cases(case):
     r = workloads.rng_for(11, 77, 0)
     launches = 1
@@ -156,8 +159,12 @@ def test_fused_edge_cases(case):
         T, H, K, E, P = 64, 1024, 16, 2048, 2
     elif case == "max_slots":  # T * K = 8192 exactly, two ranks of 256 tokens
         T, H, K, E, P = 512, 2048, 16, 64, 2
+        launches = {0: 1, 1: 2, 2: 2}  # int8 codes: the single-kernel layout, then the dispatch
+    elif case == "int8_max_slots":  # T * K = 2048 exactly: the single kernel for every mode
+        T, H, K, E, P = 128, 2048, 16, 64, 2
     elif case == "big_chunk":  # one rank of 512 tokens in one launch (workgroups of 2 tokens each)
         T, H, K, E, P = 512, 2048, 16, 64, 1
+        launches = {0: 1, 1: 2, 2: 2}
     elif case == "ragged_chunks":  # 100 tokens per rank: single-launch workgroups of 32, 32, 32, 4 tokens
         T, H, K, E, P = 200, 512, 6, 40, 2
     elif case == "big_world":  # T * K above the single-launch bound: two layout launches + dispatch
@@ -180,7 +187,8 @@ def test_fused_edge_cases(case):
     smooth = r.uniform(0.5, 1.5, (E, H) if case in ("wide_E", "per_expert_share") else H).astype(np.float32)
     for qm in (0, 1, 2):
         n = check_fused(T, H, K, E, P, 0, 0, 0, topk, None, x, w, qm, smooth if qm else None, label=case)
-        assert n == (launches if T else 1)
+        want = launches[qm] if isinstance(launches, dict) else launches
+        assert n == (want if T else 1)
 
 
 @pytest.mark.parametrize("T", [128, 4096])  # the single kernel, and the layout kernels + dispatch
@@ -190,7 +198,7 @@ def test_fused_graph_replays_match_eager(T):
     inp = workloads.make_inputs(2, seed=6, T=T, P=None if T == 4096 else 1)
     c = inp["cfg"]
     shape = mg.make_shape(c["T"], c["H"], c["K"], c["E"], c["P"], num_max=c["num_max"])
-    print(f"[fused graph] T={c['T']} P={c['P']} launches={mg.layout_dispatch_launches(shape)}", flush=True)
+    print(f"[fused graph] T={c['T']} P={c['P']} launches={mg.layout_dispatch_launches(shape, 2)}", flush=True)
     tk, xd, sd, wd = G.dev(inp["topk_idx"]), G.dev(inp["x"]), G.dev(inp["smooth"]), G.dev(inp["topk_weights"])
     lay, ex, ds, ew, cap = _outs(shape, 2, 0, c["H"])
     call = mg.prepare_layout_dispatch(shape, 2, xd, tk, None, sd, wd, out=lay, expand_x=ex, dynamic_scales=ds,
