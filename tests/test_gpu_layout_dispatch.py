@@ -150,6 +150,17 @@ def test_fused_named_workloads(cid, T, P, launches):
                 label=f"workload {cid} ({c['name']})", expect_launches=launches)
 
 
+@pytest.mark.parametrize("qm", [1, 2])
+def test_fused_full_size_per_expert_scales(qm):
+    # the decode workload (T=4096, H=7168, top-8) with [E, H] scales: the layout kernels read the
+    # token rows ahead, then the per-expert dispatch kernel
+    inp = workloads.make_inputs(2, seed=8)
+    c = inp["cfg"]
+    smooth = workloads.rng_for(8, 2, 4).uniform(0.5, 1.5, (c["E"], c["H"])).astype(np.float32)
+    check_fused(c["T"], c["H"], c["K"], c["E"], c["P"], 0, 0, 0, inp["topk_idx"], None, inp["x"],
+                inp["topk_weights"], qm, smooth, c["num_max"], label="decode, [E, H] scales", expect_launches=3)
+
+
 @pytest.mark.parametrize("case", ["wide_E", "max_slots", "int8_max_slots", "big_chunk", "ragged_chunks", "big_world",
                                   "ragged_H", "max_H", "empty", "per_expert_share", "ragged_read_ahead"])
 def test_fused_edge_cases(case):

@@ -455,14 +455,19 @@ def test_two_launch_layout_split_chunks(P, BS, K, E, Z, stride):
     G.assert_layout_equal(g, lo)
 
 
-@pytest.mark.parametrize("qm", [1, 2])
-def test_per_expert_smooth_scales_full_size(qm):
-    # the decode workload with [E, H] smooth scales (each copy quantized with its expert's row)
+@pytest.mark.parametrize("qm,kind", [(1, "expert"), (2, "expert"), (1, "channel")])
+def test_per_expert_smooth_scales_full_size(qm, kind):
+    # the decode workload with [E, H] smooth scales (each copy quantized with its expert's row), and
+    # static codes with its [H] vector: at this size (58.7 MB of x) static codes run moe_dispatch's
+    # read-ahead pass before the dispatch kernel
     inp = workloads.make_inputs(2, seed=5)
     c = inp["cfg"]
-    smooth = workloads.rng_for(5, 2, 4).uniform(0.5, 1.5, (c["E"], c["H"])).astype(np.float32)
+    if kind == "expert":
+        smooth = workloads.rng_for(5, 2, 4).uniform(0.5, 1.5, (c["E"], c["H"])).astype(np.float32)
+    else:
+        smooth = inp["smooth"]
     y_fn = lambda lo, do: workloads.expert_out_normal(lo["num_rows"], c["H"], seed=5)
     g, o = G.run_case(c["T"], c["H"], c["K"], c["E"], c["P"], 0, 0, 0, inp["topk_idx"], None, inp["x"],
                       inp["topk_weights"], qm, smooth, y_fn, num_max=c["num_max"],
-                      label=f"per-expert smooth, quant {qm}")
+                      label=f"{kind} smooth, quant {qm}")
     G.assert_case(g, o, qm)
