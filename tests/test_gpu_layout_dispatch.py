@@ -140,7 +140,7 @@ def test_fused_fuzz_worlds_two_launch(seed):
 # two layout kernels, with the read-ahead, then the dispatch (3)
 @pytest.mark.parametrize("cid,T,P,launches", [(2, 128, 1, 1), (2, 1024, None, 2), (2, None, None, 3),
                                               (3, 1024, None, 1), (3, None, None, 3), (4, 512, None, 1),
-                                              (5, 1024, None, 2),
+                                              (4, None, None, 3), (5, 1024, None, 2), (5, None, None, 3),
                                               (1, None, None, 1)])
 def test_fused_named_workloads(cid, T, P, launches):
     inp = workloads.make_inputs(cid, seed=3, T=T, P=P)
